@@ -1,0 +1,250 @@
+/*
+ * Plain fp64 CPU oracle of the dropless sparse-MoE forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or
+ * load this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code, header or table with the HIP
+ * library, and it is deliberately slow and obvious: straight loops, fp64
+ * arithmetic, no blocking, no fusion, no reordering of any sum.
+ *
+ * Sources (web pages on ScatterMoE and related kernels):
+ *  - ScatterMoE Guide (aifetchly blog), section "1. The Dynamic Routing
+ *    Imbalance Dilemma", equation H(X) = Softmax(TopK(X W_gate, k)).
+ *  - same page, section "2. Grouped Coordinate Indexing Without Padding",
+ *    the Histogram(e) and Offsets(e) equations, and section "2. The Complete
+ *    ParallelLinear PyTorch Layer" (sort of the flattened routes by expert).
+ *  - same page, section "1. The Anatomy of ParallelLinear" (gather rows of X
+ *    by index, multiply by the expert's W, scale by the router coefficient,
+ *    accumulate into the token's output row) and section "2. The Hidden Cost
+ *    of Activation Materialization" (SwiGLU experts, scatter-add of gated
+ *    expert outputs back to token order).
+ *  - Fast-LLM pull request "Add scalable sparse map kernel", section
+ *    "Testing / Correctness Validation" (unique rows inside disjoint expert
+ *    ranges, histogram counts, deterministic results).
+ *
+ * Readings where the pages leave a step open (each is also listed with the
+ * design notes):
+ *  - top-k order is descending logit, ties go to the lower expert id;
+ *  - softmax is taken over the k selected logits (equal to softmax over all
+ *    E followed by top-k and renormalisation);
+ *  - h = SiLU(x W1[e]) * (x W3[e]), y = h W2[e], with W stored
+ *    [E, D_in, D_out] row-major; the router coefficient multiplies y once,
+ *    after the nonlinearity;
+ *  - the sparse map is the stable (flat route index order) sort by expert.
+ *
+ * Inputs are raw bf16 bit patterns (uint16); each one is widened exactly to
+ * fp64 before use. Every dot product is summed in ascending index order.
+ *
+ * Parity pins: every function here is pinned by the CPU test suite (brute
+ * force, library sort, closed forms and invariants); none is unpinned.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ---------------------------------------------------------------- route -- */
+
+/* Router logits of one token: l[e] = sum_d x[d] * W_gate[d, e]. */
+static void token_logits(const uint16_t *x_row, const uint16_t *wg, int64_t D, int64_t E, double *l) {
+    for (int64_t e = 0; e < E; ++e) l[e] = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+        double xv = bf16_to_double(x_row[d]);
+        const uint16_t *wrow = wg + d * E;
+        for (int64_t e = 0; e < E; ++e) l[e] += xv * bf16_to_double(wrow[e]);
+    }
+}
+
+/* Top-k by repeated arg-max: descending logit, ties to the lower id. */
+static void token_topk(const double *l, int64_t E, int64_t k, int32_t *ids, unsigned char *taken) {
+    memset(taken, 0, (size_t)E);
+    for (int64_t j = 0; j < k; ++j) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || l[e] > l[best]) best = e;
+        }
+        taken[best] = 1;
+        ids[j] = (int32_t)best;
+    }
+}
+
+/* Softmax over the k selected logits (max subtracted). */
+static void token_softmax(const double *l, const int32_t *ids, int64_t k, double *w) {
+    double m = l[ids[0]];
+    for (int64_t j = 1; j < k; ++j)
+        if (l[ids[j]] > m) m = l[ids[j]];
+    double z = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+        w[j] = exp(l[ids[j]] - m);
+        z += w[j];
+    }
+    for (int64_t j = 0; j < k; ++j) w[j] /= z;
+}
+
+/*
+ * Router: H(X) = Softmax(TopK(X W_gate, k)).
+ * x [S, D], wg [D, E] (bf16 bits) -> ids [S, k], weights [S, k] fp64,
+ * and, when logits != NULL, the fp64 logits [S, E].
+ * If ids_in != NULL the top-k step is skipped and those ids are used
+ * (the weights are then the softmax over the given experts' logits).
+ */
+int oracle_route(const uint16_t *x, const uint16_t *wg, int64_t S, int64_t D, int64_t E, int64_t k,
+                 const int32_t *ids_in, int32_t *ids, double *weights, double *logits) {
+    if (S < 0 || D < 1 || E < 1 || k < 1 || k > E) return 1;
+    double *l = (double *)malloc(sizeof(double) * (size_t)E);
+    unsigned char *taken = (unsigned char *)malloc((size_t)E);
+    if (!l || !taken) { free(l); free(taken); return 2; }
+    for (int64_t s = 0; s < S; ++s) {
+        token_logits(x + s * D, wg, D, E, l);
+        if (logits) memcpy(logits + s * E, l, sizeof(double) * (size_t)E);
+        if (ids_in) {
+            memcpy(ids + s * k, ids_in + s * k, sizeof(int32_t) * (size_t)k);
+        } else {
+            token_topk(l, E, k, ids + s * k, taken);
+        }
+        token_softmax(l, ids + s * k, k, weights + s * k);
+    }
+    free(l);
+    free(taken);
+    return 0;
+}
+
+/* ----------------------------------------------------------- sparse map -- */
+
+/*
+ * Stable counting sort of the flat routes f = s*k + j by expert id.
+ *   counts[e]  = Histogram(e) = #{f : ids[f] = e}
+ *   offsets[e] = Offsets(e) = sum_{e' < e} counts[e'], offsets[E] = S*k
+ *   slot(f)    = offsets[ids[f]] + #{f' < f : ids[f'] = ids[f]}
+ *   sparse_rows[f] = slot(f), slot_src[slot(f)] = f
+ * Returns 1 if an id is out of range.
+ */
+int oracle_sparse_map(const int32_t *ids, int64_t S, int64_t k, int64_t E, int32_t *counts,
+                      int32_t *offsets, int32_t *sparse_rows, int32_t *slot_src) {
+    int64_t n = S * k;
+    for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t f = 0; f < n; ++f) {
+        if (ids[f] < 0 || ids[f] >= E) return 1;
+        counts[ids[f]] += 1;
+    }
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    if (!next) return 2;
+    for (int64_t e = 0; e < E; ++e) next[e] = offsets[e];
+    for (int64_t f = 0; f < n; ++f) {
+        int32_t slot = next[ids[f]]++;
+        sparse_rows[f] = slot;
+        slot_src[slot] = (int32_t)f;
+    }
+    free(next);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ ffn -- */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * One SwiGLU expert on one token row:
+ *   a = x W1[e], b = x W3[e]  (length F), h = SiLU(a) * b, y = h W2[e] (length D)
+ * w1e, w3e [D, F], w2e [F, D]; a, b, y are caller scratch.
+ */
+static void expert_row(const uint16_t *x_row, const uint16_t *w1e, const uint16_t *w3e,
+                       const uint16_t *w2e, int64_t D, int64_t F, double *a, double *b, double *y) {
+    for (int64_t f = 0; f < F; ++f) { a[f] = 0.0; b[f] = 0.0; }
+    for (int64_t d = 0; d < D; ++d) {
+        double xv = bf16_to_double(x_row[d]);
+        const uint16_t *r1 = w1e + d * F, *r3 = w3e + d * F;
+        for (int64_t f = 0; f < F; ++f) {
+            a[f] += xv * bf16_to_double(r1[f]);
+            b[f] += xv * bf16_to_double(r3[f]);
+        }
+    }
+    for (int64_t f = 0; f < F; ++f) a[f] = silu(a[f]) * b[f]; /* a now holds h */
+    for (int64_t n = 0; n < D; ++n) y[n] = 0.0;
+    for (int64_t f = 0; f < F; ++f) {
+        double hv = a[f];
+        const uint16_t *r2 = w2e + f * D;
+        for (int64_t n = 0; n < D; ++n) y[n] += hv * bf16_to_double(r2[n]);
+    }
+}
+
+typedef struct {
+    const uint16_t *x, *w1, *w3, *w2;
+    const int32_t *ids;
+    const double *weights;
+    int64_t D, F, E, k;
+    const int64_t *tokens;
+    int64_t t_begin, t_end;
+    double *out;
+    int status;
+} ffn_job;
+
+static void *ffn_worker(void *arg) {
+    ffn_job *jb = (ffn_job *)arg;
+    int64_t D = jb->D, F = jb->F, k = jb->k;
+    double *a = (double *)malloc(sizeof(double) * (size_t)F);
+    double *b = (double *)malloc(sizeof(double) * (size_t)F);
+    double *y = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!a || !b || !y) { jb->status = 2; free(a); free(b); free(y); return NULL; }
+    for (int64_t i = jb->t_begin; i < jb->t_end; ++i) {
+        int64_t s = jb->tokens[i];
+        double *o = jb->out + i * D;
+        for (int64_t n = 0; n < D; ++n) o[n] = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t e = jb->ids[s * k + j];
+            if (e < 0 || e >= jb->E) { jb->status = 1; continue; }
+            expert_row(jb->x + s * D, jb->w1 + e * D * F, jb->w3 + e * D * F, jb->w2 + e * F * D, D, F, a, b, y);
+            double g = jb->weights[s * k + j];
+            for (int64_t n = 0; n < D; ++n) o[n] += g * y[n];
+        }
+    }
+    free(a); free(b); free(y);
+    return NULL;
+}
+
+/*
+ * Dropless MoE FFN with weighted combine, for a list of tokens:
+ *   out[i, :] = sum_{j=0..k-1} weights[s, j] * SwiGLU_{ids[s, j]}(x[s, :]),  s = tokens[i]
+ * summed in j order. x [S, D]; w1, w3 [E, D, F]; w2 [E, F, D] (bf16 bits);
+ * ids [S, k]; weights [S, k] fp64; out [ntok, D] fp64.
+ * Work is split over `nthreads` POSIX threads by token; each output element
+ * is still summed in the order above.
+ */
+int oracle_ffn_tokens(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                      const int32_t *ids, const double *weights, int64_t D, int64_t F, int64_t E,
+                      int64_t k, const int64_t *tokens, int64_t ntok, double *out, int nthreads) {
+    if (D < 1 || F < 1 || E < 1 || k < 1 || ntok < 0) return 1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > ntok) nthreads = ntok > 0 ? (int)ntok : 1;
+    ffn_job *jobs = (ffn_job *)calloc((size_t)nthreads, sizeof(ffn_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return 2; }
+    int64_t per = (ntok + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        ffn_job *jb = &jobs[t];
+        jb->x = x; jb->w1 = w1; jb->w3 = w3; jb->w2 = w2; jb->ids = ids; jb->weights = weights;
+        jb->D = D; jb->F = F; jb->E = E; jb->k = k; jb->tokens = tokens; jb->out = out;
+        jb->t_begin = t * per;
+        jb->t_end = jb->t_begin + per < ntok ? jb->t_begin + per : ntok;
+        if (jb->t_begin > jb->t_end) jb->t_begin = jb->t_end;
+    }
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, ffn_worker, &jobs[t]);
+    ffn_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    int st = 0;
+    for (int t = 0; t < nthreads; ++t)
+        if (jobs[t].status) st = jobs[t].status;
+    free(jobs); free(th);
+    return st;
+}

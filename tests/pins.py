@@ -1,0 +1,223 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each pin takes an `oracle.Oracle` instance and raises AssertionError when the
+oracle disagrees with what the pages or the mathematics fix:
+
+  * brute force: every expert on every token in fp64 numpy (dense matmuls),
+    masked by the gate matrix (ScatterMoE guide, "1. The Anatomy of
+    ParallelLinear" and "2. The Hidden Cost of Activation Materialization");
+  * a library routine: the sparse map equals numpy's stable argsort by expert,
+    and offsets equal the exclusive cumulative sum of numpy's bincount (guide,
+    "2. Grouped Coordinate Indexing Without Padding", Histogram/Offsets
+    equations); the Fast-LLM correctness list (unique rows, rows inside
+    disjoint expert ranges, histogram counts, determinism);
+  * the router H(X) = Softmax(TopK(X W_gate, k)) against numpy argsort of
+    numpy logits and scipy's softmax; k = E gives the full softmax; exact
+    ties go to the lower expert id;
+  * closed forms: E = 1, k = 1 is the dense SwiGLU FFN; experts that share
+    their weights give the dense SwiGLU FFN for any routing whose gates sum
+    to one;
+  * exact invariances: token permutation, expert relabelling, scaling of W2
+    and of the gates by two.
+
+The module is also run against deliberately broken copies of the oracle
+(tests/test_oracle_mutants.py) to show that each plausible mistake fails
+at least one pin.
+"""
+from __future__ import annotations
+
+import numpy as np
+import scipy.special
+import torch
+
+import workloads as wl
+
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    return wl.bf16_bits(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16))
+
+
+def bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def small_problem(S=48, D=64, F=96, E=8, k=2, seed=0, gate_std=None, shared_experts=False):
+    """Random bf16 problem (bit arrays) small enough for brute force."""
+    rng = np.random.default_rng(seed)
+    x = bf16_bits_from_f32(rng.standard_normal((S, D)))
+    wg = bf16_bits_from_f32(rng.standard_normal((D, E)) * (gate_std or D ** -0.5))
+    if shared_experts:
+        w1 = np.broadcast_to(bf16_bits_from_f32(rng.standard_normal((D, F)) * D ** -0.5), (E, D, F)).copy()
+        w3 = np.broadcast_to(bf16_bits_from_f32(rng.standard_normal((D, F)) * D ** -0.5), (E, D, F)).copy()
+        w2 = np.broadcast_to(bf16_bits_from_f32(rng.standard_normal((F, D)) * F ** -0.5), (E, F, D)).copy()
+    else:
+        w1 = bf16_bits_from_f32(rng.standard_normal((E, D, F)) * D ** -0.5)
+        w3 = bf16_bits_from_f32(rng.standard_normal((E, D, F)) * D ** -0.5)
+        w2 = bf16_bits_from_f32(rng.standard_normal((E, F, D)) * F ** -0.5)
+    return dict(x=x, wg=wg, w1=w1, w3=w3, w2=w2, k=k, E=E)
+
+
+def dense_swiglu(x, w1, w3, w2):
+    """Textbook SwiGLU FFN in fp64 numpy: (SiLU(x W1) * (x W3)) W2."""
+    a = x @ w1
+    b = x @ w3
+    return (a * scipy.special.expit(a) * b) @ w2
+
+
+def brute_force_layer(p, ids, weights):
+    """Run every expert on every token and mask by the dense gate matrix."""
+    x = bits_to_f64(p["x"])
+    S = x.shape[0]
+    E = p["E"]
+    G = np.zeros((S, E))
+    for j in range(ids.shape[1]):
+        G[np.arange(S), ids[:, j]] += weights[:, j]
+    out = np.zeros((S, x.shape[1]))
+    for e in range(E):
+        ye = dense_swiglu(x, bits_to_f64(p["w1"][e]), bits_to_f64(p["w3"][e]), bits_to_f64(p["w2"][e]))
+        out += G[:, e:e + 1] * ye
+    return out
+
+
+def rel_err(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# --------------------------------------------------------------------- pins --
+
+def pin_router_library(o, seed=1):
+    """ids = stable argsort of -logits (library), gates = scipy softmax of the chosen logits."""
+    for (S, D, E, k) in [(64, 96, 8, 2), (40, 64, 16, 4), (30, 32, 64, 8)]:
+        p = small_problem(S=S, D=D, F=32, E=E, k=k, seed=seed + E)
+        ids, w, logits = o.route(p["x"], p["wg"], k)
+        ref_logits = bits_to_f64(p["x"]) @ bits_to_f64(p["wg"])
+        assert np.allclose(logits, ref_logits, rtol=1e-12, atol=1e-12), "router logits"
+        ref_ids = np.argsort(-ref_logits, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref_ids), "router top-k ids"
+        ref_w = scipy.special.softmax(np.take_along_axis(ref_logits, ref_ids, 1), axis=1)
+        assert np.allclose(w, ref_w, rtol=1e-12, atol=1e-14), "router gates"
+        assert np.allclose(w.sum(1), 1.0, atol=1e-14), "gates sum to one"
+        assert np.all(np.diff(w, axis=1) <= 0), "gates descending"
+        assert all(len(set(r)) == k for r in ids.tolist()), "distinct experts per token"
+
+
+def pin_router_full_softmax(o, seed=2):
+    """k = E: the gates are the full softmax over all experts, sorted descending."""
+    p = small_problem(S=20, D=48, F=16, E=6, k=6, seed=seed)
+    ids, w, logits = o.route(p["x"], p["wg"], 6)
+    full = scipy.special.softmax(bits_to_f64(p["x"]) @ bits_to_f64(p["wg"]), axis=1)
+    assert np.allclose(np.take_along_axis(full, ids, 1), w, rtol=1e-12, atol=1e-15)
+    assert np.allclose(np.sort(full, axis=1)[:, ::-1], w, rtol=1e-12, atol=1e-15)
+
+
+def pin_router_ties(o, seed=3):
+    """Exactly tied logits (duplicated W_gate columns) go to the lower expert id."""
+    rng = np.random.default_rng(seed)
+    D, E = 32, 8
+    base = rng.standard_normal((D, 4)) * 0.2
+    wg = bf16_bits_from_f32(np.concatenate([base, base], axis=1))  # expert e and e+4 tie
+    x = bf16_bits_from_f32(rng.standard_normal((16, D)))
+    ids, w, _ = o.route(x, wg, 2)
+    for r, wr in zip(ids, w):
+        assert r[0] < 4 and r[1] == r[0] + 4, "tie must rank the lower id first"
+        assert abs(wr[0] - 0.5) < 1e-15 and abs(wr[1] - 0.5) < 1e-15
+
+
+def pin_router_given_ids(o, seed=4):
+    """With ids supplied, the gates are the softmax of exactly those logits."""
+    p = small_problem(S=24, D=40, F=16, E=8, k=3, seed=seed)
+    ids_in = wl.gen_random_ids(24, 3, 8, seed=seed)
+    ids, w, logits = o.route(p["x"], p["wg"], 3, ids_in=ids_in)
+    assert np.array_equal(ids, ids_in)
+    ref_w = scipy.special.softmax(np.take_along_axis(logits, ids_in, 1), axis=1)
+    assert np.allclose(w, ref_w, rtol=1e-12, atol=1e-15)
+
+
+def check_map(ids, E, counts, offsets, rows, src):
+    flat = np.ascontiguousarray(ids).reshape(-1)
+    n = flat.size
+    ref_src = np.argsort(flat, kind="stable").astype(np.int32)
+    assert np.array_equal(src, ref_src), "slot_src = stable argsort by expert"
+    ref_counts = np.bincount(flat, minlength=E).astype(np.int32)
+    assert np.array_equal(counts, ref_counts), "histogram"
+    assert offsets[0] == 0 and np.array_equal(offsets[1:], np.cumsum(ref_counts)), "offsets"
+    assert np.array_equal(np.sort(rows), np.arange(n)), "sparse rows unique (a permutation)"
+    assert np.array_equal(rows[src], np.arange(n)), "sparse_rows and slot_src are inverse"
+    assert np.all(rows >= offsets[flat]) and np.all(rows < offsets[flat + 1]), "rows inside expert range"
+    assert np.all(np.diff(offsets) >= 0) and offsets[-1] == n, "ranges disjoint and covering"
+
+
+def pin_sparse_map(o, seed=5):
+    """Stable counting sort = numpy stable argsort; Fast-LLM invariants; E sweeps; edge cases."""
+    cases = []
+    for E in (4, 8, 16, 32, 64, 96, 128, 256):
+        k = min(4, E)
+        cases.append((wl.gen_random_ids(257, k, E, seed=seed + E), E))
+        cases.append((wl.gen_random_ids(301, k, E, seed=seed + 7 * E, skew=1.2), E))
+    cases.append((wl.gen_random_ids(128, 4, 128, seed=9), 128))  # GPT-OSS: 128 experts, 4 per token
+    cases.append((np.zeros((0, 2), np.int32), 8))  # no tokens
+    cases.append((np.array([[3, 1]], np.int32), 8))  # one token
+    cases.append((np.full((50, 1), 5, np.int32), 8))  # all on one expert, others empty
+    cases.append((np.tile(np.arange(6, dtype=np.int32), (9, 1)), 6))  # k = E
+    for ids, E in cases:
+        a = o.sparse_map(ids, E)
+        check_map(ids, E, *a)
+        b = o.sparse_map(ids, E)
+        assert all(np.array_equal(u, v) for u, v in zip(a, b)), "deterministic"
+
+
+def pin_brute_force(o, seed=6):
+    """Per-token oracle = every expert on every token, masked by the gate matrix."""
+    for (E, k) in [(8, 2), (4, 4), (16, 3)]:
+        p = small_problem(S=40, D=64, F=96, E=E, k=k, seed=seed + E)
+        ids, w, _ = o.route(p["x"], p["wg"], k)
+        out = o.ffn(p["x"], p["w1"], p["w3"], p["w2"], ids, w, nthreads=3)
+        ref = brute_force_layer(p, ids, w)
+        assert rel_err(out, ref) < 1e-12, f"brute force E={E} k={k}: {rel_err(out, ref)}"
+
+
+def pin_dense_single_expert(o, seed=7):
+    """E = 1, k = 1: the layer is the dense SwiGLU FFN."""
+    p = small_problem(S=33, D=64, F=80, E=1, k=1, seed=seed)
+    ids, w, _ = o.route(p["x"], p["wg"], 1)
+    assert np.all(ids == 0) and np.all(w == 1.0)
+    out = o.ffn(p["x"], p["w1"], p["w3"], p["w2"], ids, w)
+    ref = dense_swiglu(bits_to_f64(p["x"]), bits_to_f64(p["w1"][0]), bits_to_f64(p["w3"][0]),
+                       bits_to_f64(p["w2"][0]))
+    assert rel_err(out, ref) < 1e-12
+
+
+def pin_shared_experts(o, seed=8):
+    """Experts sharing their weights give the dense FFN for any routing (gates sum to one)."""
+    p = small_problem(S=36, D=48, F=64, E=8, k=3, seed=seed, shared_experts=True)
+    dense = dense_swiglu(bits_to_f64(p["x"]), bits_to_f64(p["w1"][0]), bits_to_f64(p["w3"][0]),
+                         bits_to_f64(p["w2"][0]))
+    ids, w, _ = o.route(p["x"], p["wg"], 3)
+    assert rel_err(o.ffn(p["x"], p["w1"], p["w3"], p["w2"], ids, w), dense) < 1e-12
+    zid = wl.gen_random_ids(36, 3, 8, seed=seed, skew=1.2)
+    zw = np.random.default_rng(seed).dirichlet(np.ones(3), size=36)
+    assert rel_err(o.ffn(p["x"], p["w1"], p["w3"], p["w2"], zid, zw), dense) < 1e-12
+
+
+def pin_invariances(o, seed=9):
+    """Exact invariances: token permutation, expert relabelling, x2 scaling of W2 and of the gates."""
+    p = small_problem(S=32, D=64, F=64, E=8, k=2, seed=seed)
+    ids, w, _ = o.route(p["x"], p["wg"], 2)
+    base = o.ffn(p["x"], p["w1"], p["w3"], p["w2"], ids, w)
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(32)
+    out = o.ffn(p["x"][perm], p["w1"], p["w3"], p["w2"], ids[perm], w[perm])
+    assert np.array_equal(out, base[perm]), "token permutation"
+    sigma = rng.permutation(8)  # new expert sigma[e] holds old expert e
+    inv = np.argsort(sigma)
+    out = o.ffn(p["x"], p["w1"][inv], p["w3"][inv], p["w2"][inv], sigma[ids].astype(np.int32), w)
+    assert np.array_equal(out, base), "expert relabelling"
+    w2x2 = bf16_bits_from_f32(bits_to_f64(p["w2"]).astype(np.float32) * 2.0)
+    assert np.array_equal(o.ffn(p["x"], p["w1"], p["w3"], w2x2, ids, w), 2.0 * base), "linear in W2"
+    assert np.array_equal(o.ffn(p["x"], p["w1"], p["w3"], p["w2"], ids, 2.0 * w), 2.0 * base), "linear in g"
+    tok = np.array([5, 0, 31, 5], dtype=np.int64)
+    assert np.array_equal(o.ffn(p["x"], p["w1"], p["w3"], p["w2"], ids, w, tokens=tok), base[tok]), "token subset"
+
+
+ALL_PINS = [pin_router_library, pin_router_full_softmax, pin_router_ties, pin_router_given_ids,
+            pin_sparse_map, pin_brute_force, pin_dense_single_expert, pin_shared_experts, pin_invariances]

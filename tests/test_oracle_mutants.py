@@ -1,0 +1,62 @@
+"""Plausible mistakes planted in copies of the oracle must each fail a pin.
+
+Each mutant is a text edit of oracle/oracle.c compiled into a temporary
+library on the CPU; the real oracle is never modified. Every edit keeps all
+memory accesses in bounds.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "gate_up_swapped": ("a[f] = silu(a[f]) * b[f];", "a[f] = silu(b[f]) * a[f];"),
+    "gate_dropped": ("o[n] += g * y[n];", "o[n] += y[n];"),
+    "gate_index_reversed": ("double g = jb->weights[s * k + j];", "double g = jb->weights[s * k + (k - 1 - j)];"),
+    "tie_to_higher_id": ("if (best < 0 || l[e] > l[best]) best = e;", "if (best < 0 || l[e] >= l[best]) best = e;"),
+    "topk_ascending": ("if (best < 0 || l[e] > l[best]) best = e;", "if (best < 0 || l[e] < l[best]) best = e;"),
+    "softmax_unnormalised": ("for (int64_t j = 0; j < k; ++j) w[j] /= z;", "for (int64_t j = 0; j < k; ++j) w[j] /= 1.0;"),
+    "softmax_missing_max_term": ("w[j] = exp(l[ids[j]] - m);", "w[j] = exp(l[ids[j]] - m) + (j == 0 ? 1e-9 : 0.0);"),
+    "w1_transposed": ("a[f] += xv * bf16_to_double(r1[f]);", "a[f] += xv * bf16_to_double(w1e[f * D + d]);"),
+    "w_gate_transposed": ("for (int64_t e = 0; e < E; ++e) l[e] += xv * bf16_to_double(wrow[e]);",
+                          "for (int64_t e = 0; e < E; ++e) l[e] += xv * bf16_to_double(wg[(e * D + d) % (D * E)]);"),
+    "down_first_term_dropped": ("for (int64_t f = 0; f < F; ++f) {\n        double hv = a[f];",
+                                "for (int64_t f = 1; f < F; ++f) {\n        double hv = a[f];"),
+    "wrong_expert_slab": ("jb->w2 + e * F * D", "jb->w2 + ((e + 1) % jb->E) * F * D"),
+    "map_unstable": ("for (int64_t f = 0; f < n; ++f) {\n        int32_t slot = next[ids[f]]++;",
+                     "for (int64_t f = n - 1; f >= 0; --f) {\n        int32_t slot = next[ids[f]]++;"),
+    "offsets_off_by_one": ("offsets[e + 1] = offsets[e] + counts[e];",
+                           "offsets[e + 1] = offsets[e] + counts[e] - (e == 0 && counts[0] > 0);"),
+    "x_row_of_wrong_token": ("expert_row(jb->x + s * D,", "expert_row(jb->x + (s > 0 && j == 1 ? s - 1 : s) * D,"),
+}
+
+
+@pytest.fixture(scope="module")
+def src_text():
+    with open(oracle.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(src_text, name):
+    old, new = MUTANTS[name]
+    assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
+    with tempfile.TemporaryDirectory() as td:
+        src = os.path.join(td, "mutant.c")
+        lib = os.path.join(td, "libmutant.so")
+        with open(src, "w") as f:
+            f.write(src_text.replace(old, new))
+        oracle.build(src=src, out=lib)
+        mut = oracle.Oracle(lib)
+        failed = []
+        for pin in pins.ALL_PINS:
+            try:
+                pin(mut)
+            except (AssertionError, ValueError, IndexError):
+                failed.append(pin.__name__)
+        assert failed, f"mutant {name} passed every pin"
