@@ -1,0 +1,186 @@
+"""Benchmark of the dropless sparse-MoE forward on one MI355X.
+
+A step is one whole forward pass on resident inputs: router top-k + softmax,
+sparse map, gathered gate+up GEMM with SwiGLU, down GEMM with weighted
+scatter-add, and the bf16 finalize -- the three C-ABI calls back to back on
+one stream. The default workload is the Mixtral-8x7B-shaped layer
+(S=4096, D=4096, F=14336, E=8, k=2) with seeded synthetic inputs.
+
+Prints one JSON line with the whole-job throughput (tokens/s), the
+roofline of the dominant kernel (timed live with HIP events on its own
+stream over the timed region) and the fp64 CPU oracle timed on a bounded
+sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "MoE-layer fwd tokens/s + % bf16 MFMA peak (Mixtral-shape, S=4096, 1 GPU)"
+KERNEL_SOURCES = ["sparse_mixture_experts_gemv_amd/csrc/gemm.hpp", "sparse_mixture_experts_gemv_amd/csrc/common.hpp",
+                  "sparse_mixture_experts_gemv_amd/csrc/ffn.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def layer_flops(S, D, F, E, k, with_router=True):
+    return 6.0 * S * k * D * F + (2.0 * S * D * E if with_router else 0.0)
+
+
+def load_traffic(workload: str, per_launch_units: float):
+    """HBM bytes per launch of the gate+up kernel from committed rocprofv3 PMC
+    counters, or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_ffn_gate_up_gemm_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, p, target_s: float = 15.0):
+    """The fp64 oracle (route + map + FFN) on a bounded sample of tokens."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as wl
+
+    o = oracle.get()
+    nthreads = min(16, os.cpu_count() or 1)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(cfg.S)
+    wg = wl.bf16_bits(p["wg"].cpu())
+    w1 = wl.bf16_bits(p["w1"].cpu())
+    w3 = wl.bf16_bits(p["w3"].cpu())
+    w2 = wl.bf16_bits(p["w2"].cpu())
+    done, t_used = 0, 0.0
+    while t_used < target_s and done < cfg.S:
+        n = min(nthreads * 2, cfg.S - done)
+        toks = np.sort(order[done:done + n])
+        x = wl.bf16_bits(p["x"][torch.from_numpy(toks).to(p["x"].device)].cpu())
+        t0 = time.perf_counter()
+        if "ids" in p:
+            ids = p["ids"].cpu().numpy()[toks]
+            w = p["weights"].cpu().numpy()[toks].astype(np.float64)
+        else:
+            ids, w, _ = o.route(x, wg, cfg.k)
+        o.sparse_map(ids, cfg.E)
+        o.ffn(x, w1, w3, w2, ids, w, nthreads=nthreads)
+        t_used += time.perf_counter() - t0
+        done += n
+    return {"value": done / t_used, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{done} random tokens of the {cfg.name} workload (route + map + FFN, fp64, "
+                      f"{nthreads} threads, {t_used:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral", help="tiny | mixtral | gptoss | dsv3 | qwen2")
+    ap.add_argument("--S", type=int, default=None, help="token count (default: the configuration's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the dropless MoE forward here runs on a single MI355X "
+              "(expert- or token-parallel sharding is described in DESIGN.md, not built). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mixture_experts_gemv_amd as smoe
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = wl.CONFIGS[args.config]
+    if args.S:
+        cfg = cfg.with_S(args.S)
+    S, D, F, E, k = cfg.S, cfg.D, cfg.F, cfg.E, cfg.k
+    print(f"bench: {cfg.describe()} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    p = wl.make_problem(cfg, S=S, device="cuda")
+    layer = smoe.MoELayer(p["wg"], p["w1"], p["w3"], p["w2"], k, S)
+    topk = (p["ids"], p["weights"]) if "ids" in p else None
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        layer.forward(p["x"], topk=topk)
+    torch.cuda.synchronize()
+
+    smoe.profile_start(args.steps * 16)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        layer.forward(p["x"], topk=topk)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    kern = smoe.profile_stop()
+    ms = t0.elapsed_time(t1) / args.steps
+
+    flops = layer_flops(S, D, F, E, k, with_router=topk is None)
+    tokens_per_s = S / (ms / 1e3)
+    kernels = {name: {"avg_us": 1e3 * tot / n, "launches": n} for name, (tot, n) in kern.items()}
+    gu_ms = kern["ffn_gate_up_gemm"][0] / kern["ffn_gate_up_gemm"][1]
+    gu_flops = 4.0 * S * k * D * F
+    achieved = gu_flops / (gu_ms / 1e3) / 1e12
+    traffic = load_traffic(cfg.name, S * k)
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} MoE layer forward (dropless, SwiGLU experts)", "S": S, "D": D, "F": F,
+                   "E": E, "k": k, "routing": "router top-k" if topk is None else "Zipf(1.2) expert draws"},
+        "layer_tflops": round(flops / (ms / 1e3) / 1e12, 1),
+        "layer_mfma_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "ffn_gate_up_gemm", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "algorithmic_flops_per_launch": gu_flops,
+                     "avg_launch_us": round(gu_ms * 1e3, 2)},
+        "kernels": {n: {"avg_us": round(v["avg_us"], 2), "launches": v["launches"]} for n, v in kernels.items()},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, p, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C ABI of the dropless sparse Mixture-of-Experts forward path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The forward pass has four stages. This library exports them as three calls:
+ *
+ *   moe_route_topk       router: H(X) = Softmax(TopK(X W_gate, k))
+ *                        (ScatterMoE Guide, section "1. The Dynamic Routing
+ *                        Imbalance Dilemma", equation H(X)).
+ *   moe_sparse_map       per-expert histogram, exclusive scan and stable
+ *                        route -> slot assignment (same page, section
+ *                        "2. Grouped Coordinate Indexing Without Padding",
+ *                        equations Histogram(e) and Offsets(e); Fast-LLM pull
+ *                        request "Add scalable sparse map kernel", sections
+ *                        "Solution" and "Usage": the (expert_ends,
+ *                        expert_pad_begins, sparse_rows) triple).
+ *   moe_scatter_ffn_fwd  SwiGLU experts over gathered token rows with no
+ *                        [S*k, D] copy and no padding, then the
+ *                        router-weighted scatter-add back to token order
+ *                        (ScatterMoE Guide, figure "The ParallelLinear Core
+ *                        Abstraction" and section "1. The Anatomy of
+ *                        ParallelLinear": ParallelLinear(X, W, I, G); section
+ *                        "2. The Hidden Cost of Activation Materialization").
+ *
+ * Notation: S tokens, D model width, F expert FFN width, E experts, k experts
+ * per token. f = s*k + j is the flat route index of token s's j-th expert. A
+ * "slot" is a row of the expert-sorted order: slots [offsets[e], offsets[e+1])
+ * belong to expert e and are ordered by f (a stable sort).
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *    tensors), row-major, 16-byte aligned. bf16 values are passed as their
+ *    raw 16-bit patterns (uint16_t).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on it, never synchronises the host and never allocates.
+ *  - The caller owns every buffer. Inputs are read only; outputs are fully
+ *    overwritten. `workspace` is caller-allocated scratch whose contents are
+ *    undefined before and after a call; calls in flight at the same time
+ *    must use different workspaces.
+ *  - Errors: argument checks happen on the host before anything is
+ *    enqueued: NULL pointer, misaligned pointer, S < 0, E < 1, k < 1, k > E
+ *    -> MOE_ERR_INVALID_ARGUMENT; shapes outside the kernels' limits ->
+ *    MOE_ERR_UNSUPPORTED; workspace too small -> MOE_ERR_WORKSPACE_TOO_SMALL;
+ *    a failed launch -> MOE_ERR_LAUNCH. S == 0 enqueues nothing (or, for the
+ *    sparse map, only the zeroing of counts and offsets) and returns MOE_OK.
+ *  - Device-side preconditions are NOT checked on the GPU: expert ids lie in
+ *    [0, E) and are distinct within a token; the map passed to
+ *    moe_scatter_ffn_fwd was built from the same ids; S*k < 2^31.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_LAUNCH = 4
+} moe_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_str(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int moe_version(void);
+
+/*
+ * Workspace bytes moe_route_topk needs for these sizes (router logits in
+ * fp32, [S, E]). Pure host function.
+ */
+size_t moe_route_workspace_bytes(int32_t S, int32_t E);
+
+/*
+ * Router (ScatterMoE Guide, section "1. The Dynamic Routing Imbalance
+ * Dilemma", equation H(X); the page's FFN block computes the same thing as
+ * softmax, top-k, renormalise).
+ *   logits[s, e] = sum_d x[s, d] * w_gate[d, e]      (bf16 in, fp32 sum)
+ *   topk_ids[s, 0..k-1]  = the k largest logits, descending; equal logits
+ *                          rank the lower expert id first
+ *   topk_weights[s, j]   = exp(l_j - l_0) / sum_j' exp(l_j' - l_0)  (fp32)
+ * x [S, D] bf16; w_gate [D, E] bf16; topk_ids [S, k] int32;
+ * topk_weights [S, k] fp32; workspace >= moe_route_workspace_bytes(S, E).
+ * Limits: D % 64 == 0, E % 8 == 0, E <= 256, k <= 16 (else UNSUPPORTED).
+ */
+int moe_route_topk(const uint16_t *x, const uint16_t *w_gate, int32_t S, int32_t D, int32_t E, int32_t k,
+                   int32_t *topk_ids, float *topk_weights, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/* Workspace bytes moe_sparse_map needs. Pure host function. */
+size_t moe_sparse_map_workspace_bytes(int32_t S, int32_t k, int32_t E);
+
+/*
+ * Sparse map (ScatterMoE Guide, section "2. Grouped Coordinate Indexing
+ * Without Padding"; Fast-LLM scalable sparse map):
+ *   expert_counts[e]   = Histogram(e) = #{f : topk_ids[f] == e}
+ *   expert_offsets[e]  = Offsets(e) = sum_{e' < e} expert_counts[e'];
+ *                        expert_offsets[E] = S*k. Fast-LLM's expert_ends are
+ *                        expert_offsets[1..E]; expert_pad_begins equal the
+ *                        ends (dropless: no padding).
+ *   sparse_rows[f]     = slot of route f = expert_offsets[e] +
+ *                        #{f' < f : topk_ids[f'] == e}, e = topk_ids[f]
+ *   slot_src[slot]     = f (inverse permutation of sparse_rows)
+ * The assignment is deterministic and stable (flat route order), so the
+ * result is bit-identical from run to run.
+ * topk_ids [S, k] int32 in [0, E); expert_counts [E]; expert_offsets [E+1];
+ * sparse_rows, slot_src [S*k] (all int32).
+ * Limits: E <= 1024 (else UNSUPPORTED).
+ */
+int moe_sparse_map(const int32_t *topk_ids, int32_t S, int32_t k, int32_t E, int32_t *expert_counts,
+                   int32_t *expert_offsets, int32_t *sparse_rows, int32_t *slot_src, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes moe_scatter_ffn_fwd needs: the intermediate h [S*k, F]
+ * bf16 in slot order, the fp32 combine accumulator [S, D] and a tile table.
+ * No term is proportional to S*k*D: token rows are never replicated.
+ * Pure host function.
+ */
+size_t moe_scatter_ffn_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k);
+
+/*
+ * Scattered SwiGLU experts with weighted scatter-add combine (ScatterMoE
+ * Guide, "The ParallelLinear Core Abstraction": gather rows of X by index,
+ * tile GEMM against W[e], scale by the router coefficient, accumulate into
+ * the token's output row; section "2. The Hidden Cost of Activation
+ * Materialization": SwiGLU experts).
+ * For every slot r of expert e (offsets[e] <= r < offsets[e+1]), with
+ * f = slot_src[r] and token t = f / k:
+ *   h[r, :]  = bf16( SiLU(x[t, :] W1[e]) * (x[t, :] W3[e]) )   (fp32 sums)
+ *   acc[t,:] += topk_weights[f] * (h[r, :] W2[e])               (fp32)
+ *   out[t,:]  = bf16(acc[t, :])     (round to nearest even, once)
+ * x [S, D] bf16; w1, w3 [E, D, F] bf16; w2 [E, F, D] bf16 (each expert's
+ * matrix is [D_in, D_out] with D_out contiguous); topk_weights [S, k] fp32;
+ * expert_offsets [E+1] and slot_src [S*k] from moe_sparse_map on the same
+ * ids; out [S, D] bf16 (fully written; tokens with no route get zeros).
+ * workspace >= moe_scatter_ffn_workspace_bytes(S, D, F, E, k).
+ * Limits: D % 64 == 0, F % 64 == 0, E <= 1024 (else UNSUPPORTED).
+ */
+int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                        const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                        int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Profiling hooks (measurement support, not part of the method). While
+ * enabled, every kernel launched by the calls above is bracketed by a pair of
+ * HIP events recorded on its stream.
+ *   moe_profile_start(capacity): create 2*capacity events up front and start
+ *     recording (at most `capacity` kernels are recorded; later ones are
+ *     not). Clears previous totals.
+ *   moe_profile_stop(): stop recording, wait for the recorded events and add
+ *     each kernel's elapsed time to its totals.
+ *   moe_profile_read(kernel, &name, &total_ms, &launches): totals of kernel
+ *     kind `kernel` (0 <= kernel < moe_profile_kinds()); name is a static
+ *     string.
+ * Host-side state is process-wide and guarded by a mutex.
+ */
+int moe_profile_start(int capacity);
+int moe_profile_stop(void);
+int moe_profile_kinds(void);
+int moe_profile_read(int kernel, const char **name, double *total_ms, int *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

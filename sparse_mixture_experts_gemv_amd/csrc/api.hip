@@ -1,0 +1,98 @@
+// C ABI entry points (declared and documented in include/moe.h): argument
+// validation on the host, workspace sizing and kernel launches on the
+// caller's stream. Nothing here allocates memory or synchronises the host.
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace {
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int finish(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+int moe_version(void) { return 100; }
+
+size_t moe_route_workspace_bytes(int32_t S, int32_t E) {
+    if (S < 0 || E < 1) return 0;
+    return smoe::route_ws_bytes(S, E);
+}
+
+int moe_route_topk(const uint16_t *x, const uint16_t *w_gate, int32_t S, int32_t D, int32_t E, int32_t k,
+                   int32_t *topk_ids, float *topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
+    if (S < 0 || D < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if (S == 0) return MOE_OK;
+    if (!x || !w_gate || !topk_ids || !topk_weights || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+    if (misaligned(x) || misaligned(w_gate) || misaligned(topk_ids) || misaligned(topk_weights) ||
+        misaligned(workspace))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (D % 64 != 0 || E % 8 != 0 || E > 256 || k > 16) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)S * D >= ((int64_t)1 << 31) || (int64_t)S * E >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (workspace_bytes < smoe::route_ws_bytes(S, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return finish(smoe::launch_route(x, w_gate, S, D, E, k, topk_ids, topk_weights, workspace,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t moe_sparse_map_workspace_bytes(int32_t S, int32_t k, int32_t E) {
+    if (S < 0 || k < 1 || E < 1) return 0;
+    return smoe::align_up(smoe::sparse_map_plan((int64_t)S * k, E).ws_bytes);
+}
+
+int moe_sparse_map(const int32_t *topk_ids, int32_t S, int32_t k, int32_t E, int32_t *expert_counts,
+                   int32_t *expert_offsets, int32_t *sparse_rows, int32_t *slot_src, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    if (S < 0 || k < 1 || E < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARGUMENT;
+    if (misaligned(expert_counts) || misaligned(expert_offsets)) return MOE_ERR_INVALID_ARGUMENT;
+    if (E > 1024) return MOE_ERR_UNSUPPORTED;
+    const int64_t N = (int64_t)S * k;
+    if (N >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (N > 0) {
+        if (!topk_ids || !sparse_rows || !slot_src || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+        if (misaligned(topk_ids) || misaligned(sparse_rows) || misaligned(slot_src) || misaligned(workspace))
+            return MOE_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes < smoe::sparse_map_plan(N, E).ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    }
+    return finish(smoe::launch_sparse_map(topk_ids, (int)N, E, expert_counts, expert_offsets, sparse_rows, slot_src,
+                                          workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t moe_scatter_ffn_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k) {
+    if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1) return 0;
+    return smoe::ffn_plan(S, D, F, E, k).ws_bytes;
+}
+
+int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                        const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                        int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *out, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if (S == 0) return MOE_OK;
+    if (!x || !w1 || !w3 || !w2 || !topk_weights || !expert_offsets || !slot_src || !out || !workspace)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (misaligned(x) || misaligned(w1) || misaligned(w3) || misaligned(w2) || misaligned(topk_weights) ||
+        misaligned(expert_offsets) || misaligned(slot_src) || misaligned(out) || misaligned(workspace))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (D % 64 != 0 || F % 64 != 0 || E > 1024) return MOE_ERR_UNSUPPORTED;
+    const int64_t N = (int64_t)S * k;
+    if (N >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (workspace_bytes < smoe::ffn_plan(S, D, F, E, k).ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return finish(smoe::launch_scatter_ffn(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, S, D, F, E, k, out,
+                                           workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

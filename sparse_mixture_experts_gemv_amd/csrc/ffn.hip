@@ -1,0 +1,175 @@
+// Scattered SwiGLU expert FFN with router-weighted scatter-add combine.
+//
+// ScatterMoE Guide, "The ParallelLinear Core Abstraction" and "1. The
+// Anatomy of ParallelLinear": token rows are read in place through the
+// expert-sorted index (no [S*k, D] copy), each expert's rows are cut into
+// ceil(N_e / BM) tiles with a masked last tile (no padding), the expert GEMM
+// runs per tile and the result is scaled by the router coefficient and
+// accumulated into the token's output row.
+//
+// Launch sequence on one stream (no host synchronisation):
+//   tile_table  expert offsets -> (expert, row_begin, row_end) per M tile
+//   acc_zero    fp32 accumulator [S, D] = 0
+//   gate+up     h[r] = bf16(SiLU(x[t] W1[e]) * (x[t] W3[e]))  (gathered A)
+//   down        acc[t] += w_f * (h[r] W2[e])                  (fp32 atomics)
+//   finalize    out = bf16(acc)
+#include <algorithm>
+
+#include "gemm.hpp"
+#include "launch.hpp"
+#include "profile.hpp"
+
+namespace smoe {
+
+__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restrict__ offsets, int E, int N, int bm,
+                                                          int n_mtiles, int4 *__restrict__ tiles) {
+    __shared__ int s_wave[16];
+    const int e = threadIdx.x;
+    const int lane = e & 63, w = e >> 6;
+    int off = 0, end = 0, t = 0;
+    if (e < E) {
+        off = min(max(offsets[e], 0), N);
+        end = min(max(offsets[e + 1], off), N);
+        t = (end - off + bm - 1) / bm;
+    }
+    int x = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) s_wave[w] = x;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int i = 0; i < 16; ++i) {
+        if (i < w) base += s_wave[i];
+        total += s_wave[i];
+    }
+    base += x - t;
+    for (int i = 0; i < t && base + i < n_mtiles; ++i)
+        tiles[base + i] = make_int4(e, off + i * bm, min(off + (i + 1) * bm, end), 0);
+    for (int j = total + threadIdx.x; j < n_mtiles; j += 1024) tiles[j] = make_int4(-1, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void acc_zero_kernel(float4 *__restrict__ acc, size_t n4) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__global__ __launch_bounds__(256) void acc_finalize_kernel(const float4 *__restrict__ acc, uint2 *__restrict__ out,
+                                                           size_t n4) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 v = acc[i];
+        const uint32_t lo = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
+        out[i] = make_uint2(lo, hi);
+    }
+}
+
+static int pick_bm(int64_t S, int64_t E, int64_t k) {
+    const int64_t avg = S * k / std::max<int64_t>(E, 1);
+    if (avg >= 96) return 128;
+    if (avg >= 48) return 64;
+    if (avg >= 24) return 32;
+    return 16;
+}
+
+FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
+    FfnPlan pl;
+    const int64_t N = S * k;
+    pl.bm = pick_bm(S, E, k);
+    pl.n_mtiles = (int)((N + std::min(E, N) * (pl.bm - 1)) / pl.bm);
+    size_t off = 0;
+    pl.tiles_off = off;
+    off += align_up((size_t)std::max(pl.n_mtiles, 1) * sizeof(int4));
+    pl.h_off = off;
+    off += align_up((size_t)N * (size_t)F * 2);
+    pl.acc_off = off;
+    off += align_up((size_t)S * (size_t)D * 4);
+    pl.ws_bytes = off;
+    return pl;
+}
+
+static int grid_for(size_t n, int per_block) {
+    const size_t b = (n + per_block - 1) / per_block;
+    return (int)std::min<size_t>(std::max<size_t>(b, 1), 2048);
+}
+
+template <int BM, int BN, int WM, int WN, int MODE>
+static void launch_gemm(const GemmParams &p0, hipStream_t stream) {
+    GemmParams p = p0;
+    p.n_ntiles = (p.N + BN - 1) / BN;
+    const int blocks = p.n_mtiles * p.n_ntiles;
+    if (blocks == 0) return;
+    const int kid = MODE == kGateUp ? kKGateUp : kKDown;
+    prof_begin(stream, kid);
+    grouped_gemm_kernel<BM, BN, WM, WN, MODE><<<blocks, 256, 0, stream>>>(p);
+    prof_end(stream, kid);
+}
+
+template <int MODE>
+static void launch_gemm_bm(int bm, const GemmParams &p, hipStream_t stream) {
+    switch (bm) {
+        case 128: launch_gemm<128, 128, 2, 2, MODE>(p, stream); break;
+        case 64: launch_gemm<64, 128, 2, 2, MODE>(p, stream); break;
+        case 32: launch_gemm<32, 128, 2, 2, MODE>(p, stream); break;
+        default: launch_gemm<16, 128, 1, 4, MODE>(p, stream); break;
+    }
+}
+
+hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                              const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                              int S, int D, int F, int E, int k, uint16_t *out, void *workspace,
+                              hipStream_t stream) {
+    const FfnPlan pl = ffn_plan(S, D, F, E, k);
+    char *ws = reinterpret_cast<char *>(workspace);
+    int4 *tiles = reinterpret_cast<int4 *>(ws + pl.tiles_off);
+    uint16_t *h = reinterpret_cast<uint16_t *>(ws + pl.h_off);
+    float *acc = reinterpret_cast<float *>(ws + pl.acc_off);
+    const int N = S * k;
+    const size_t n4 = (size_t)S * D / 4;
+
+    prof_begin(stream, kKTileTable);
+    tile_table_kernel<<<1, 1024, 0, stream>>>(expert_offsets, E, N, pl.bm, pl.n_mtiles, tiles);
+    prof_end(stream, kKTileTable);
+    prof_begin(stream, kKAccZero);
+    acc_zero_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<float4 *>(acc), n4);
+    prof_end(stream, kKAccZero);
+
+    GemmParams p{};
+    p.slot_src = slot_src;
+    p.gate = topk_weights;
+    p.tiles = tiles;
+    p.topk = k;
+    p.n_mtiles = pl.n_mtiles;
+    p.group_m = 8;
+
+    // gate + up: A = gathered token rows of x, K = D, N = F
+    p.A = x;
+    p.B0 = w1;
+    p.B1 = w3;
+    p.C = h;
+    p.M = N;
+    p.N = F;
+    p.K = D;
+    launch_gemm_bm<kGateUp>(pl.bm, p, stream);
+
+    // down + scatter-add: A = h (slot order), K = F, N = D
+    p.A = h;
+    p.B0 = w2;
+    p.B1 = nullptr;
+    p.C = acc;
+    p.N = D;
+    p.K = F;
+    launch_gemm_bm<kDown>(pl.bm, p, stream);
+
+    prof_begin(stream, kKFinalize);
+    acc_finalize_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
+                                                                    reinterpret_cast<uint2 *>(out), n4);
+    prof_end(stream, kKFinalize);
+    return hipGetLastError();
+}
+
+}  // namespace smoe

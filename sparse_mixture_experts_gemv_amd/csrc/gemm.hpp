@@ -1,0 +1,254 @@
+// Grouped, gathered bf16 GEMM tile kernel for gfx950 (MFMA 16x16x32).
+//
+// One workgroup (4 waves) computes a BM x BN output tile of one expert:
+//   C[r, n] = sum_k A[row(r), k] * B_e[k, n]
+// where rows r are slots [row_begin, row_end) of that expert (from a tile
+// table built from the scanned expert offsets) and row(r) is either the slot
+// itself (contiguous A) or the token of the slot (gathered A: token rows of
+// X read in place, never copied).
+//
+// Three epilogues:
+//   kGateUp   two B matrices (W1, W3) share every A tile; the tile writes
+//             h = bf16(SiLU(A W1) * (A W3)) in slot order (fused gate+up).
+//   kDown     one B matrix (W2); the tile scales each row by its route's
+//             router weight and atomically adds into the fp32 token
+//             accumulator (scatter-add combine).
+//   kLogits   one B matrix (W_gate), no experts; fp32 store (router logits).
+//
+// Weights are [E, K, N] with N contiguous. MFMA wants K-contiguous operands,
+// so each thread loads an 8x8 block of B (8 rows of 16 B), transposes it in
+// registers and writes 8 K-contiguous 16 B chunks to LDS. Both A and B live
+// in LDS as rows of 64 K values (BK = 64) with an XOR chunk swizzle, double
+// buffered: global loads for step k+1 are in flight while step k computes.
+#pragma once
+
+#include "common.hpp"
+
+namespace smoe {
+
+enum GemmMode { kGateUp = 0, kDown = 1, kLogits = 2 };
+
+struct GemmParams {
+    const uint16_t *A;        // X [S, K] (kGateUp, kLogits) or h [S*k, K] (kDown)
+    const uint16_t *B0;       // W1 / W2 / W_gate: [E, K, N]
+    const uint16_t *B1;       // W3 (kGateUp only)
+    const int32_t *slot_src;  // [S*k] slot -> flat route index
+    const float *gate;        // [S*k] router weights (kDown)
+    const int4 *tiles;        // [n_mtiles] (expert, row_begin, row_end, -) ; expert < 0 = empty
+    void *C;                  // h bf16 [S*k, N] / acc fp32 [S, N] / logits fp32 [S, N]
+    int M;                    // rows (kLogits: S)
+    int N;                    // output columns
+    int K;                    // reduction length (multiple of 64)
+    int topk;                 // k (token = flat route index / k)
+    int n_mtiles;
+    int n_ntiles;
+    int group_m;              // M tiles per tile group (L2 reuse order)
+};
+
+template <int BM, int BN, int WM, int WN, int MODE>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams p) {
+    constexpr int NB = (MODE == kGateUp) ? 2 : 1;
+    constexpr int BK = 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int MT = WTM / 16, NT = WTN / 16;
+    static_assert(WM * WN == 4, "4 waves per workgroup");
+    static_assert(MT >= 1 && NT >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be 16-aligned");
+    constexpr int A_BYTES = BM * BK * 2;
+    constexpr int B_BYTES = BN * BK * 2;
+    constexpr int STAGE = A_BYTES + NB * B_BYTES;
+    constexpr int A_CHUNKS = BM * 8;             // 16 B chunks per A stage
+    constexpr int A_ITERS = (A_CHUNKS + 255) / 256;
+    constexpr int B_BLOCKS = NB * BN;            // 8x8 blocks per B stage (BK/8 * BN/8 * NB)
+    constexpr int B_ITERS = (B_BLOCKS + 255) / 256;
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // ---- tile decode: XCD-contiguous logical id, grouped M-major order ----
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_group = p.group_m * p.n_ntiles;
+    const int grp = L / per_group;
+    const int within = L - grp * per_group;
+    const int m_first = grp * p.group_m;
+    const int gm = min(p.group_m, p.n_mtiles - m_first);
+    const int nt = within / gm;
+    const int mt = m_first + (within - nt * gm);
+
+    int expert, row0, row1;
+    if (MODE == kLogits) {
+        expert = 0;
+        row0 = mt * BM;
+        row1 = min(p.M, row0 + BM);
+    } else {
+        const int4 t = p.tiles[mt];
+        expert = t.x;
+        row0 = t.y;
+        row1 = t.z;
+    }
+    if (expert < 0 || row0 >= row1) return;
+    const int n0 = nt * BN;
+    const int N = p.N, K = p.K;
+    const size_t b_off = (size_t)expert * (size_t)K * (size_t)N;
+
+    // ---- A loader: thread -> (row, chunk), row pointer fixed for the tile ----
+    const uint16_t *a_src[A_ITERS];
+    int a_lds[A_ITERS];
+#pragma unroll
+    for (int i = 0; i < A_ITERS; ++i) {
+        const int idx = tid + 256 * i;
+        const int r = idx >> 3, c = idx & 7;
+        int slot = row0 + (r < BM ? r : 0);
+        if (slot >= row1) slot = row1 - 1;  // rows past the expert's end load a valid row, never stored
+        long arow;
+        if (MODE == kGateUp) arow = p.slot_src[slot] / p.topk;
+        else arow = slot;
+        a_src[i] = p.A + arow * (long)K + c * 8;
+        a_lds[i] = lds_off(r, c);
+    }
+    // ---- B loader: thread -> 8x8 block (k rows kb*8.., n cols nb*8..) ----
+    const uint16_t *b_src[B_ITERS];
+    int b_lds_row[B_ITERS];
+    int b_kb[B_ITERS];
+    bool b_ok[B_ITERS];
+#pragma unroll
+    for (int i = 0; i < B_ITERS; ++i) {
+        const int blk = tid + 256 * i;
+        const int kb = blk & 7, nb = blk >> 3;
+        const int which = nb / (BN / 8);
+        const int ncol = (nb % (BN / 8)) * 8;
+        const uint16_t *base = (NB == 2 && which == 1) ? p.B1 : p.B0;
+        b_ok[i] = (blk < B_BLOCKS) && (n0 + ncol < N);
+        b_src[i] = base + b_off + (size_t)(kb * 8) * N + (b_ok[i] ? n0 + ncol : 0);
+        b_lds_row[i] = which * BN + ncol;  // first LDS row (n) of the block, within the B region
+        b_kb[i] = kb;
+    }
+
+    uint4 ra[A_ITERS];
+    uint4 rb[B_ITERS][8];
+
+    auto load_global = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i)
+            if (A_CHUNKS % 256 == 0 || tid + 256 * i < A_CHUNKS)
+                ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + kt * BK);
+#pragma unroll
+        for (int i = 0; i < B_ITERS; ++i) {
+            const uint16_t *src = b_src[i] + (size_t)kt * BK * N;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (b_ok[i]) rb[i][r] = *reinterpret_cast<const uint4 *>(src + (size_t)r * N);
+                else rb[i][r] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto store_lds = [&](int stage) {
+        char *sa = smem + stage * STAGE;
+        char *sb = sa + A_BYTES;
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i)
+            if (A_CHUNKS % 256 == 0 || tid + 256 * i < A_CHUNKS)
+                *reinterpret_cast<uint4 *>(sa + a_lds[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_ITERS; ++i) {
+            if (B_BLOCKS % 256 == 0 || tid + 256 * i < B_BLOCKS) {
+                uint4 t[8];
+                transpose8x8(rb[i], t);
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    *reinterpret_cast<uint4 *>(sb + lds_off(b_lds_row[i] + c, b_kb[i])) = t[c];
+            }
+        }
+    };
+
+    f32x4 acc[NB][MT][NT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = K / BK;
+    load_global(0);
+    store_lds(0);
+    __syncthreads();
+
+    const int frag_row = lane & 15;
+    const int frag_chunk = lane >> 4;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int stage = kt & 1;
+        if (kt + 1 < KT) load_global(kt + 1);
+        const char *sa = smem + stage * STAGE;
+        const char *sb = sa + A_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            uint4 af[MT];
+            uint4 bfr[NB][NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                af[i] = *reinterpret_cast<const uint4 *>(sa + lds_off(wm * WTM + i * 16 + frag_row, kk * 4 + frag_chunk));
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    bfr[b][j] = *reinterpret_cast<const uint4 *>(
+                        sb + b * B_BYTES + lds_off(wn * WTN + j * 16 + frag_row, kk * 4 + frag_chunk));
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) acc[b][i][j] = mfma_16x16x32(af[i], bfr[b][j], acc[b][i][j]);
+        }
+        if (kt + 1 < KT) store_lds(stage ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue ----
+    const int col_in_tile = lane & 15;
+    const int row_grp = (lane >> 4) * 4;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = wm * WTM + i * 16 + row_grp + r;
+            const int slot = row0 + row;
+            if (slot >= row1) continue;
+            if (MODE == kGateUp) {
+                uint16_t *h = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) {
+                        const float g = acc[0][i][j][r], u = acc[1][i][j][r];
+                        const float s = g / (1.0f + __expf(-g));
+                        h[col] = f32_to_bf16_bits(s * u);
+                    }
+                }
+            } else if (MODE == kDown) {
+                const int f = p.slot_src[slot];
+                const int tok = f / p.topk;
+                const float w = p.gate[f];
+                float *accp = reinterpret_cast<float *>(p.C) + (size_t)tok * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) atomicAdd(accp + col, w * acc[0][i][j][r]);
+                }
+            } else {
+                float *out = reinterpret_cast<float *>(p.C) + (size_t)slot * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) out[col] = acc[0][i][j][r];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace smoe

@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, validates arguments before touching the GPU, and sizes its
+workspaces without any [S*k, D] term. No kernel is launched here."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import sparse_mixture_experts_gemv_amd as smoe
+    return smoe.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    import sparse_mixture_experts_gemv_amd._lib as b
+    names = header_functions()
+    assert len(names) == 12, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(b.SIGNATURES)
+
+
+def test_status_strings(lib):
+    import sparse_mixture_experts_gemv_amd as smoe
+    assert smoe.status_str(0) == "MOE_OK"
+    assert smoe.status_str(1) == "MOE_ERR_INVALID_ARGUMENT"
+    assert smoe.status_str(2) == "MOE_ERR_UNSUPPORTED"
+    assert smoe.status_str(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
+    assert smoe.status_str(4) == "MOE_ERR_LAUNCH"
+    assert smoe.status_str(99) == "MOE_ERR_UNKNOWN"
+    assert lib.moe_version() >= 100
+
+
+# a non-NULL, 16-byte aligned host address: never dereferenced, because every
+# call below fails validation before anything is enqueued
+FAKE = ctypes.c_void_p(0x100000)
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+def test_route_validation(lib):
+    r = lib.moe_route_topk
+    assert r(FAKE, FAKE, 16, 64, 8, 0, FAKE, FAKE, FAKE, 1 << 20, None) == 1  # k < 1
+    assert r(FAKE, FAKE, 16, 64, 8, 9, FAKE, FAKE, FAKE, 1 << 20, None) == 1  # k > E
+    assert r(FAKE, FAKE, -1, 64, 8, 2, FAKE, FAKE, FAKE, 1 << 20, None) == 1  # S < 0
+    assert r(None, FAKE, 16, 64, 8, 2, FAKE, FAKE, FAKE, 1 << 20, None) == 1  # NULL
+    assert r(MISALIGNED, FAKE, 16, 64, 8, 2, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert r(FAKE, FAKE, 16, 96, 8, 2, FAKE, FAKE, FAKE, 1 << 20, None) == 2  # D % 64
+    assert r(FAKE, FAKE, 16, 64, 12, 2, FAKE, FAKE, FAKE, 1 << 20, None) == 2  # E % 8
+    assert r(FAKE, FAKE, 16, 64, 512, 2, FAKE, FAKE, FAKE, 1 << 20, None) == 2  # E > 256
+    assert r(FAKE, FAKE, 16, 64, 8, 2, FAKE, FAKE, FAKE, 16, None) == 3  # workspace
+    assert r(None, None, 0, 64, 8, 2, None, None, None, 0, None) == 0  # S == 0: no-op
+
+
+def test_sparse_map_validation(lib):
+    m = lib.moe_sparse_map
+    assert m(FAKE, 16, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1  # E < 1
+    assert m(FAKE, 16, 3, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1  # k > E
+    assert m(FAKE, 16, 2, 8, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert m(FAKE, 16, 2, 8, FAKE, FAKE, FAKE, MISALIGNED, FAKE, 1 << 20, None) == 1
+    assert m(FAKE, 16, 2, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 2  # E > 1024
+    assert m(FAKE, 1 << 30, 4, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 2  # S*k >= 2^31
+    assert m(FAKE, 4096, 2, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == 3
+
+
+def test_ffn_validation(lib):
+    f = lib.moe_scatter_ffn_fwd
+    args = lambda S=16, D=64, F=128, E=8, k=2, ws=1 << 30, x=FAKE: (
+        x, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, S, D, F, E, k, FAKE, FAKE, ws, None)
+    assert f(*args(k=9)) == 1
+    assert f(*args(x=None)) == 1
+    assert f(*args(x=MISALIGNED)) == 1
+    assert f(*args(D=80)) == 2
+    assert f(*args(F=100)) == 2
+    assert f(*args(E=2048, k=2)) == 2
+    assert f(*args(ws=1024)) == 3
+    assert f(None, None, None, None, None, None, None, 0, 64, 128, 8, 2, None, None, 0, None) == 0
+
+
+def test_workspace_has_no_token_replication(lib):
+    """Closed form on the ScatterMoE guide's pipeline figure: replicating the
+    tokens costs S*k*D*2 bytes (67.1 MB at S=D=4096, k=2, fp16; 2.15 GB over
+    32 layers). The FFN workspace grows with D only through the fp32 [S, D]
+    accumulator, never through an [S*k, D] term."""
+    fig = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
+    rep = fig["replication_bytes_per_layer"]
+    nbytes = rep["S"] * rep["k"] * rep["D"] * rep["bytes_per_element"]
+    assert round(nbytes / 1e6, 1) == rep["value_MB"]
+    assert round(32 * nbytes / 1e9, 2) == fig["replication_bytes_32_layers"]["value_GB"]
+    oh = fig["one_hot_register_elements"]
+    assert oh["block_size"] * oh["num_experts"] == oh["value"]
+    ws = lambda S, D, F, E, k: lib.moe_scatter_ffn_workspace_bytes(S, D, F, E, k)
+    for (S, F, E, k) in [(4096, 14336, 8, 2), (4096, 2048, 256, 8), (8192, 2880, 128, 4)]:
+        d1, d2 = ws(S, 4096, F, E, k), ws(S, 8192, F, E, k)
+        assert d2 - d1 == S * 4096 * 4  # fp32 accumulator only
+        # h [S*k, F] bf16 + acc [S, D] fp32 + a small tile table (alignment slack)
+        base = S * k * F * 2 + S * 4096 * 4
+        assert base <= d1 <= base + 64 * 1024
+    # the router and map workspaces do not scale with D at all
+    assert lib.moe_route_workspace_bytes(4096, 256) == 4096 * 256 * 4
+    assert lib.moe_sparse_map_workspace_bytes(4096, 8, 256) < 1 << 20
+
+
+def test_product_path_does_not_use_oracle():
+    """The package must not import or load the oracle or fall back to the CPU."""
+    pkg = os.path.join(ROOT, "sparse_mixture_experts_gemv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.lower(), f"{fn} mentions the oracle"

@@ -1,0 +1,110 @@
+"""moe_scatter_ffn_fwd and the whole forward pass on the GPU against the fp64 oracle.
+
+Small shapes are compared element by element over every token; they cover
+each M-tile size the launcher picks (16, 32, 64, 128 rows), ragged N tiles
+(F or D not a multiple of 128), ragged M tails and empty experts. The five
+configurations run at their full sizes with the launch configuration of the
+benchmark, and sampled tokens are checked one by one against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import DEV, assert_close, make_problem, oracle_ffn_rows, sample_tokens, say
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_ffn(p, ids, weights):
+    import sparse_mixture_experts_gemv_amd as smoe
+    _, offsets, _, src = smoe.moe_sparse_map(ids, p["cfg"].E)
+    out = smoe.moe_scatter_ffn_fwd(p["x"], p["w1"], p["w3"], p["w2"], weights, offsets, src)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def routing_for(p, seed):
+    cfg, S = p["cfg"], p["S"]
+    if "ids" in p:
+        return p["ids"], p["weights"]
+    ids = wl.gen_random_ids(S, cfg.k, cfg.E, seed=seed)
+    w = np.random.default_rng(seed).dirichlet(np.ones(cfg.k), size=S).astype(np.float32)
+    return torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+
+
+SMALL = [  # (S, D, F, E, k): tile size picked from S*k/E
+    (1000, 192, 320, 8, 2),    # 250 rows/expert -> 128-row tiles, F ragged
+    (300, 128, 192, 8, 2),     # 75 -> 64-row tiles
+    (200, 128, 256, 16, 2),    # 25 -> 32-row tiles
+    (40, 256, 128, 64, 8),     # 5 -> 16-row tiles, many empty experts
+    (64, 2880, 2880, 128, 4),  # GPT-OSS widths: D and F = 45 * 64
+    (33, 320, 192, 4, 1),      # k = 1
+    (1, 64, 64, 8, 2),         # one token
+]
+
+
+@pytest.mark.parametrize("S,D,F,E,k", SMALL)
+def test_ffn_small_all_tokens(oracle_lib, S, D, F, E, k):
+    cfg = wl.MoEConfig("small", 50 + E + k, S, D, F, E, k, None)
+    p = make_problem(cfg)
+    ids, w = routing_for(p, seed=S + E)
+    got = gpu_ffn(p, ids, w)
+    ref = oracle_ffn_rows(oracle_lib, p, ids.cpu().numpy(), w.cpu().numpy(), np.arange(S))
+    assert_close(got, ref, f"ffn {S}x{D}x{F} E={E} k={k}", configured=False)
+
+
+def test_ffn_skewed_single_expert(oracle_lib):
+    """All routes on two experts: one expert spans many M tiles, the rest are empty."""
+    cfg = wl.MoEConfig("skew", 61, 700, 128, 192, 16, 2, None)
+    p = make_problem(cfg)
+    ids = np.tile(np.array([[3, 11]], np.int32), (700, 1))
+    w = np.random.default_rng(0).dirichlet(np.ones(2), size=700).astype(np.float32)
+    got = gpu_ffn(p, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+    ref = oracle_ffn_rows(oracle_lib, p, ids, w, np.arange(700))
+    assert_close(got, ref, "two hot experts", configured=False)
+
+
+def full_layer(oracle_lib, cfg, S=None, n_sample=24):
+    import sparse_mixture_experts_gemv_amd as smoe
+    p = make_problem(cfg, S=S)
+    S = p["S"]
+    layer = smoe.MoELayer(p["wg"], p["w1"], p["w3"], p["w2"], cfg.k, S)
+    topk = (p["ids"], p["weights"]) if "ids" in p else None
+    out = layer.forward(p["x"], topk=topk)
+    torch.cuda.synchronize()
+    out2 = layer.forward(p["x"], topk=topk)  # repeat: same map, same result within fp32 atomics jitter
+    torch.cuda.synchronize()
+    ids = (p["ids"] if topk else layer.ids).cpu().numpy()
+    got = out.float().cpu().numpy().astype(np.float64)
+    tokens = sample_tokens(S, n_sample, seed=cfg.cfg_id + S)
+    if topk:
+        weights = p["weights"].cpu().numpy().astype(np.float64)
+    else:  # oracle conditioned on the GPU's ids: fp64 softmax over those experts' logits
+        _, weights_t, _ = oracle_lib.route(wl.bf16_bits(p["x"][torch.from_numpy(tokens).to(DEV)].cpu()),
+                                           wl.bf16_bits(p["wg"].cpu()), cfg.k, ids_in=ids[tokens])
+        weights = np.zeros((S, cfg.k))
+        weights[tokens] = weights_t
+    # the map of the full run is bit-exact against the oracle's
+    smap = [t.cpu().numpy() for t in layer.map]
+    ref_map = oracle_lib.sparse_map(ids, cfg.E)
+    for g, r in zip(smap, ref_map):
+        assert np.array_equal(g, r)
+    ref = oracle_ffn_rows(oracle_lib, p, ids, weights, tokens)
+    m = assert_close(got[tokens], ref, f"{cfg.name} S={S} ({len(tokens)} sampled tokens)")
+    d = np.abs(out2.float().cpu().numpy() - got).max()
+    assert d <= (0 if cfg.k <= 2 else 2e-2), d
+    return m
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "gptoss", "dsv3"])
+def test_layer_full_size(oracle_lib, name):
+    cfg = wl.CONFIGS[name]
+    say(f"layer {cfg.describe()}")
+    full_layer(oracle_lib, cfg, n_sample=cfg.S if name == "tiny" else 24)
+
+
+@pytest.mark.parametrize("S", wl.QWEN2_BATCHES)
+def test_layer_qwen2_zipf(oracle_lib, S):
+    cfg = wl.CONFIGS["qwen2"]
+    say(f"layer {cfg.with_S(S).describe()}")
+    full_layer(oracle_lib, cfg, S=S, n_sample=min(S, 24))

@@ -1,0 +1,97 @@
+"""moe_sparse_map on the GPU: bit-exact against the oracle's stable counting
+sort, on the configurations' expert counts, the Fast-LLM expert-count sweeps
+(4..32 and 64..256), large route counts and the degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import DEV, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_map(ids_np, E):
+    import sparse_mixture_experts_gemv_amd as smoe
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(DEV)
+    out = smoe.moe_sparse_map(ids, E)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+def check_exact(oracle_lib, ids, E, what):
+    say(f"  map {what}: S={ids.shape[0]} k={ids.shape[1]} E={E}")
+    got = run_map(ids, E)
+    ref = oracle_lib.sparse_map(ids, E)
+    for name, g, r in zip(("counts", "offsets", "sparse_rows", "slot_src"), got, ref):
+        assert np.array_equal(g, r), f"{what}: {name} differs at {np.nonzero(g != r)[0][:8]}"
+    return got
+
+
+@pytest.mark.parametrize("E", [4, 8, 16, 32, 64, 96, 128, 256, 1024])
+@pytest.mark.parametrize("skew", [None, 1.2])
+def test_expert_sweep(oracle_lib, E, skew):
+    for S, k in [(1, 1), (7, 2), (1000, min(4, E)), (8192, min(8, E))]:
+        ids = wl.gen_random_ids(S, k, E, seed=E * 31 + S, skew=skew)
+        check_exact(oracle_lib, ids, E, f"sweep skew={skew}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "gptoss", "dsv3", "qwen2"])
+def test_config_shapes(oracle_lib, name):
+    cfg = wl.CONFIGS[name]
+    if cfg.routing == "zipf":
+        for S in wl.QWEN2_BATCHES:
+            ids, _ = wl.gen_zipf_routing(cfg, S)
+            check_exact(oracle_lib, ids, cfg.E, f"{name} S={S}")
+    else:
+        ids = wl.gen_random_ids(cfg.S, cfg.k, cfg.E, seed=cfg.cfg_id)
+        check_exact(oracle_lib, ids, cfg.E, name)
+
+
+def test_gptoss_router_ids(oracle_lib):
+    """GPT-OSS shape: ids from the softmax of random router logits, map bit-exact."""
+    import sparse_mixture_experts_gemv_amd as smoe
+    cfg = wl.CONFIGS["gptoss"]
+    x = wl.gen_x(cfg).to(DEV)
+    wg = wl.gen_w_gate(cfg).to(DEV)
+    ids, _ = smoe.moe_route_topk(x, wg, cfg.k)
+    torch.cuda.synchronize()
+    check_exact(oracle_lib, ids.cpu().numpy(), cfg.E, "gptoss router ids")
+
+
+@pytest.mark.parametrize("S", [1 << 16, 1 << 19, 1 << 21])
+def test_large(oracle_lib, S):
+    ids = wl.gen_random_ids(S, 4, 128, seed=S)
+    check_exact(oracle_lib, ids, 128, "large")
+
+
+def test_degenerate(oracle_lib):
+    check_exact(oracle_lib, np.full((5000, 1), 3, np.int32), 8, "all on one expert")
+    check_exact(oracle_lib, np.tile(np.arange(8, dtype=np.int32), (333, 1)), 8, "k = E")
+    check_exact(oracle_lib, np.array([[5, 2]], np.int32), 8, "one token")
+    check_exact(oracle_lib, np.array([[0]], np.int32), 1, "E = 1")
+    ids = wl.gen_random_ids(777, 2, 4, seed=1)
+    check_exact(oracle_lib, (ids * 37 + 5).astype(np.int32), 160, "sparse expert set")
+    counts, offsets, _, _ = run_map(np.zeros((0, 2), np.int32), 8)
+    assert not counts.any() and not offsets.any()
+
+
+def test_invalid_ids_get_no_slot(oracle_lib):
+    ids = wl.gen_random_ids(300, 2, 8, seed=3)
+    bad = ids.copy()
+    bad[10, 1] = 8
+    bad[20, 0] = -1
+    counts, offsets, rows, src = run_map(bad, 8)
+    assert rows[21] == -1 and rows[40] == -1
+    keep = np.ones(600, bool)
+    keep[[21, 40]] = False
+    ref_src = np.nonzero(keep)[0][np.argsort(bad.ravel()[keep], kind="stable")]
+    assert offsets[-1] == 598 and np.array_equal(src[:598], ref_src)
+
+
+def test_deterministic():
+    ids = wl.gen_random_ids(32768, 8, 256, seed=11)
+    a = run_map(ids, 256)
+    for _ in range(3):
+        b = run_map(ids, 256)
+        assert all(np.array_equal(u, v) for u, v in zip(a, b))

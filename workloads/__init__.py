@@ -150,6 +150,28 @@ def gen_random_ids(S: int, k: int, E: int, seed: int, skew: Optional[float] = No
     return out
 
 
+def make_problem(cfg: MoEConfig, S: Optional[int] = None, device="cuda", gen_device=None) -> dict:
+    """All inputs of `cfg` (optionally with another token count) on `device`.
+
+    Small problems are drawn on the CPU; large ones are drawn on `device`
+    (the values then differ from a CPU draw, but every consumer -- the HIP
+    path and, through host copies, the oracle -- reads the same tensors).
+    """
+    S = cfg.S if S is None else S
+    if gen_device is None:
+        big = cfg.E * cfg.D * cfg.F > (1 << 26)
+        gen_device = device if big else "cpu"
+    x = gen_x(cfg, gen_device, S=S).to(device)
+    wg = gen_w_gate(cfg, gen_device).to(device)
+    w1, w3, w2 = (t.to(device) for t in gen_expert_weights(cfg, gen_device))
+    p = dict(cfg=cfg, S=S, x=x, wg=wg, w1=w1, w3=w3, w2=w2)
+    if cfg.routing == "zipf":
+        ids, w = gen_zipf_routing(cfg, S)
+        p["ids"] = torch.from_numpy(ids).to(device)
+        p["weights"] = torch.from_numpy(w).to(device)
+    return p
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a (CPU) bf16 tensor as a uint16 numpy array."""
     assert t.dtype == torch.bfloat16
