@@ -87,7 +87,8 @@ size_t moe_route_workspace_bytes(int32_t S, int32_t E);
  *   topk_weights[s, j]   = exp(l_j - l_0) / sum_j' exp(l_j' - l_0)  (fp32)
  * x [S, D] bf16; w_gate [D, E] bf16; topk_ids [S, k] int32;
  * topk_weights [S, k] fp32; workspace >= moe_route_workspace_bytes(S, E).
- * Limits: D % 64 == 0, E % 8 == 0, E <= 256, k <= 16 (else UNSUPPORTED).
+ * Limits: D % 64 == 0, E % 8 == 0, E <= 256, k <= 16, S*D < 2^30
+ * (else UNSUPPORTED).
  */
 int moe_route_topk(const uint16_t *x, const uint16_t *w_gate, int32_t S, int32_t D, int32_t E, int32_t k,
                    int32_t *topk_ids, float *topk_weights, void *workspace, size_t workspace_bytes,
@@ -141,7 +142,8 @@ size_t moe_scatter_ffn_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t 
  * expert_offsets [E+1] and slot_src [S*k] from moe_sparse_map on the same
  * ids; out [S, D] bf16 (fully written; tokens with no route get zeros).
  * workspace >= moe_scatter_ffn_workspace_bytes(S, D, F, E, k).
- * Limits: D % 64 == 0, F % 64 == 0, E <= 1024 (else UNSUPPORTED).
+ * Limits: D % 64 == 0, F % 64 == 0, E <= 1024, S*D < 2^30, D*F < 2^30
+ * (32-bit buffer offsets; else UNSUPPORTED).
  */
 int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                         const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,

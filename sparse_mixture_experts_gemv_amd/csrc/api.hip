@@ -41,7 +41,7 @@ int moe_route_topk(const uint16_t *x, const uint16_t *w_gate, int32_t S, int32_t
         misaligned(workspace))
         return MOE_ERR_INVALID_ARGUMENT;
     if (D % 64 != 0 || E % 8 != 0 || E > 256 || k > 16) return MOE_ERR_UNSUPPORTED;
-    if ((int64_t)S * D >= ((int64_t)1 << 31) || (int64_t)S * E >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)S * D >= ((int64_t)1 << 30) || (int64_t)S * E >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (workspace_bytes < smoe::route_ws_bytes(S, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     return finish(smoe::launch_route(x, w_gate, S, D, E, k, topk_ids, topk_weights, workspace,
                                      reinterpret_cast<hipStream_t>(stream)));
@@ -89,7 +89,9 @@ int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
         return MOE_ERR_INVALID_ARGUMENT;
     if (D % 64 != 0 || F % 64 != 0 || E > 1024) return MOE_ERR_UNSUPPORTED;
     const int64_t N = (int64_t)S * k;
-    if (N >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    // 32-bit buffer offsets: x, each expert matrix and each tile's rows of h stay below 2 GiB
+    if (N >= ((int64_t)1 << 31) || (int64_t)S * D >= ((int64_t)1 << 30) || (int64_t)D * F >= ((int64_t)1 << 30))
+        return MOE_ERR_UNSUPPORTED;
     if (workspace_bytes < smoe::ffn_plan(S, D, F, E, k).ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
     return finish(smoe::launch_scatter_ffn(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, S, D, F, E, k, out,
                                            workspace, reinterpret_cast<hipStream_t>(stream)));

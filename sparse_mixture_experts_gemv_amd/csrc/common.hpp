@@ -57,6 +57,17 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
     }
 }
 
+// Buffer resource over [base, base + bytes): loads past the end return zero
+// instead of faulting. Word 3 is the CDNA raw-buffer format (32-bit data,
+// no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin by block index. Map
 // physical block ids so that each XCD receives one contiguous range of
 // logical tile ids: neighbouring tiles then share that XCD's L2.

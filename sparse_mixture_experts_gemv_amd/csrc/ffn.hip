@@ -16,39 +16,56 @@
 #include <algorithm>
 
 #include "gemm.hpp"
+#include "gemm_pp.hpp"
 #include "launch.hpp"
 #include "profile.hpp"
 
 namespace smoe {
 
-__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restrict__ offsets, int E, int N, int bm,
-                                                          int n_mtiles, int4 *__restrict__ tiles) {
-    __shared__ int s_wave[16];
+// One thread per expert: ceil(rows / bm) tiles each, exclusive scan over the
+// experts, then every expert writes its (expert, row_begin, row_end) entries.
+// Two tile heights are handled in one launch (one per GEMM); entries past the
+// real tile count are marked empty (expert = -1).
+__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restrict__ offsets, int E, int N, int bm0,
+                                                          int n0, int4 *__restrict__ tiles0, int bm1, int n1,
+                                                          int4 *__restrict__ tiles1) {
+    __shared__ int s_wave[2][16];
     const int e = threadIdx.x;
     const int lane = e & 63, w = e >> 6;
-    int off = 0, end = 0, t = 0;
+    int off = 0, end = 0;
     if (e < E) {
         off = min(max(offsets[e], 0), N);
         end = min(max(offsets[e + 1], off), N);
-        t = (end - off + bm - 1) / bm;
     }
-    int x = t;
+    const int bms[2] = {bm0, bm1};
+    const int ns[2] = {n0, n1};
+    int4 *const tabs[2] = {tiles0, tiles1};
+    int t[2], x[2];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
+    for (int q = 0; q < 2; ++q) {
+        t[q] = (e < E) ? (end - off + bms[q] - 1) / bms[q] : 0;
+        x[q] = t[q];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x[q], d);
+            if (lane >= d) x[q] += y;
+        }
+        if (lane == 63) s_wave[q][w] = x[q];
     }
-    if (lane == 63) s_wave[w] = x;
     __syncthreads();
-    int base = 0, total = 0;
-    for (int i = 0; i < 16; ++i) {
-        if (i < w) base += s_wave[i];
-        total += s_wave[i];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if (tabs[q] == nullptr) continue;
+        int base = 0, total = 0;
+        for (int i = 0; i < 16; ++i) {
+            if (i < w) base += s_wave[q][i];
+            total += s_wave[q][i];
+        }
+        base += x[q] - t[q];
+        for (int i = 0; i < t[q] && base + i < ns[q]; ++i)
+            tabs[q][base + i] = make_int4(e, off + i * bms[q], min(off + (i + 1) * bms[q], end), 0);
+        for (int j = total + threadIdx.x; j < ns[q]; j += 1024) tabs[q][j] = make_int4(-1, 0, 0, 0);
     }
-    base += x - t;
-    for (int i = 0; i < t && base + i < n_mtiles; ++i)
-        tiles[base + i] = make_int4(e, off + i * bm, min(off + (i + 1) * bm, end), 0);
-    for (int j = total + threadIdx.x; j < n_mtiles; j += 1024) tiles[j] = make_int4(-1, 0, 0, 0);
 }
 
 __global__ __launch_bounds__(256) void acc_zero_kernel(float4 *__restrict__ acc, size_t n4) {
@@ -68,22 +85,38 @@ __global__ __launch_bounds__(256) void acc_finalize_kernel(const float4 *__restr
     }
 }
 
-static int pick_bm(int64_t S, int64_t E, int64_t k) {
-    const int64_t avg = S * k / std::max<int64_t>(E, 1);
-    if (avg >= 96) return 128;
-    if (avg >= 48) return 64;
-    if (avg >= 24) return 32;
-    return 16;
+// Kernel choice per GEMM from the mean rows per expert (known on the host
+// without reading the device-side counts):
+//   >= 192 rows: ping-pong LDS-DMA kernel, 256-row tiles
+//   >=  96 rows: ping-pong LDS-DMA kernel, 128-row tiles
+//   fewer:       register-staged kernel with 64 / 32 / 16-row tiles
+enum GemmKind { kKindReg = 0, kKindPP = 1 };
+
+static void pick_gemm(int64_t avg, int &kind, int &bm) {
+    if (avg >= 192) { kind = kKindPP; bm = 256; }
+    else if (avg >= 96) { kind = kKindPP; bm = 128; }
+    else if (avg >= 48) { kind = kKindReg; bm = 64; }
+    else if (avg >= 24) { kind = kKindReg; bm = 32; }
+    else { kind = kKindReg; bm = 16; }
+}
+
+static int tiles_upper_bound(int64_t N, int64_t E, int bm) {
+    return (int)((N + std::min(E, N) * (bm - 1)) / bm);
 }
 
 FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
     FfnPlan pl;
     const int64_t N = S * k;
-    pl.bm = pick_bm(S, E, k);
-    pl.n_mtiles = (int)((N + std::min(E, N) * (pl.bm - 1)) / pl.bm);
+    const int64_t avg = N / std::max<int64_t>(E, 1);
+    pick_gemm(avg, pl.kind_up, pl.bm_up);
+    pick_gemm(avg, pl.kind_down, pl.bm_down);
+    pl.n_mtiles_up = tiles_upper_bound(N, E, pl.bm_up);
+    pl.n_mtiles_down = tiles_upper_bound(N, E, pl.bm_down);
     size_t off = 0;
-    pl.tiles_off = off;
-    off += align_up((size_t)std::max(pl.n_mtiles, 1) * sizeof(int4));
+    pl.tiles_up_off = off;
+    off += align_up((size_t)std::max(pl.n_mtiles_up, 1) * sizeof(int4));
+    pl.tiles_down_off = off;
+    off += align_up((size_t)std::max(pl.n_mtiles_down, 1) * sizeof(int4));
     pl.h_off = off;
     off += align_up((size_t)N * (size_t)F * 2);
     pl.acc_off = off;
@@ -98,25 +131,43 @@ static int grid_for(size_t n, int per_block) {
 }
 
 template <int BM, int BN, int WM, int WN, int MODE>
-static void launch_gemm(const GemmParams &p0, hipStream_t stream) {
+static void launch_reg(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
     p.n_ntiles = (p.N + BN - 1) / BN;
     const int blocks = p.n_mtiles * p.n_ntiles;
     if (blocks == 0) return;
-    const int kid = MODE == kGateUp ? kKGateUp : kKDown;
-    prof_begin(stream, kid);
     grouped_gemm_kernel<BM, BN, WM, WN, MODE><<<blocks, 256, 0, stream>>>(p);
-    prof_end(stream, kid);
+}
+
+template <int BM, int BN, int MODE, int BK, int STAGES>
+static void launch_pp(const GemmParams &p0, hipStream_t stream) {
+    GemmParams p = p0;
+    p.n_ntiles = (p.N + BN - 1) / BN;
+    const int blocks = p.n_mtiles * p.n_ntiles;
+    if (blocks == 0) return;
+    grouped_gemm_pp_kernel<BM, BN, MODE, BK, STAGES><<<blocks, 512, 0, stream>>>(p);
 }
 
 template <int MODE>
-static void launch_gemm_bm(int bm, const GemmParams &p, hipStream_t stream) {
-    switch (bm) {
-        case 128: launch_gemm<128, 128, 2, 2, MODE>(p, stream); break;
-        case 64: launch_gemm<64, 128, 2, 2, MODE>(p, stream); break;
-        case 32: launch_gemm<32, 128, 2, 2, MODE>(p, stream); break;
-        default: launch_gemm<16, 128, 1, 4, MODE>(p, stream); break;
+static void launch_gemm(int kind, int bm, const GemmParams &p, hipStream_t stream) {
+    const int kid = MODE == kGateUp ? kKGateUp : kKDown;
+    prof_begin(stream, kid);
+    if (kind == kKindPP) {
+        if constexpr (MODE == kGateUp) {
+            if (bm == 256) launch_pp<256, 128, MODE, 64, 2>(p, stream);
+            else launch_pp<128, 128, MODE, 32, 5>(p, stream);
+        } else {
+            if (bm == 256) launch_pp<256, 256, MODE, 32, 5>(p, stream);
+            else launch_pp<128, 256, MODE, 64, 3>(p, stream);
+        }
+    } else {
+        switch (bm) {
+            case 64: launch_reg<64, 128, 2, 2, MODE>(p, stream); break;
+            case 32: launch_reg<32, 128, 2, 2, MODE>(p, stream); break;
+            default: launch_reg<16, 128, 1, 4, MODE>(p, stream); break;
+        }
     }
+    prof_end(stream, kid);
 }
 
 hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
@@ -125,14 +176,16 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
                               hipStream_t stream) {
     const FfnPlan pl = ffn_plan(S, D, F, E, k);
     char *ws = reinterpret_cast<char *>(workspace);
-    int4 *tiles = reinterpret_cast<int4 *>(ws + pl.tiles_off);
+    int4 *tiles_up = reinterpret_cast<int4 *>(ws + pl.tiles_up_off);
+    int4 *tiles_down = reinterpret_cast<int4 *>(ws + pl.tiles_down_off);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + pl.h_off);
     float *acc = reinterpret_cast<float *>(ws + pl.acc_off);
     const int N = S * k;
     const size_t n4 = (size_t)S * D / 4;
 
     prof_begin(stream, kKTileTable);
-    tile_table_kernel<<<1, 1024, 0, stream>>>(expert_offsets, E, N, pl.bm, pl.n_mtiles, tiles);
+    tile_table_kernel<<<1, 1024, 0, stream>>>(expert_offsets, E, N, pl.bm_up, pl.n_mtiles_up, tiles_up, pl.bm_down,
+                                              pl.n_mtiles_down, tiles_down);
     prof_end(stream, kKTileTable);
     prof_begin(stream, kKAccZero);
     acc_zero_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<float4 *>(acc), n4);
@@ -141,12 +194,13 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     GemmParams p{};
     p.slot_src = slot_src;
     p.gate = topk_weights;
-    p.tiles = tiles;
     p.topk = k;
-    p.n_mtiles = pl.n_mtiles;
+    p.A_rows = S;
     p.group_m = 8;
 
     // gate + up: A = gathered token rows of x, K = D, N = F
+    p.tiles = tiles_up;
+    p.n_mtiles = pl.n_mtiles_up;
     p.A = x;
     p.B0 = w1;
     p.B1 = w3;
@@ -154,16 +208,18 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.M = N;
     p.N = F;
     p.K = D;
-    launch_gemm_bm<kGateUp>(pl.bm, p, stream);
+    launch_gemm<kGateUp>(pl.kind_up, pl.bm_up, p, stream);
 
     // down + scatter-add: A = h (slot order), K = F, N = D
+    p.tiles = tiles_down;
+    p.n_mtiles = pl.n_mtiles_down;
     p.A = h;
     p.B0 = w2;
     p.B1 = nullptr;
     p.C = acc;
     p.N = D;
     p.K = F;
-    launch_gemm_bm<kDown>(pl.bm, p, stream);
+    launch_gemm<kDown>(pl.kind_down, pl.bm_down, p, stream);
 
     prof_begin(stream, kKFinalize);
     acc_finalize_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),

@@ -20,6 +20,9 @@
 // registers and writes 8 K-contiguous 16 B chunks to LDS. Both A and B live
 // in LDS as rows of 64 K values (BK = 64) with an XOR chunk swizzle, double
 // buffered: global loads for step k+1 are in flight while step k computes.
+// All global reads are buffer loads: rows past the end of a buffer read as
+// zero, and rows or columns outside the tile only feed outputs that are
+// never stored, so the loads need no per-element masking.
 #pragma once
 
 #include "common.hpp"
@@ -36,7 +39,8 @@ struct GemmParams {
     const float *gate;        // [S*k] router weights (kDown)
     const int4 *tiles;        // [n_mtiles] (expert, row_begin, row_end, -) ; expert < 0 = empty
     void *C;                  // h bf16 [S*k, N] / acc fp32 [S, N] / logits fp32 [S, N]
-    int M;                    // rows (kLogits: S)
+    int M;                    // rows (kLogits: S); A has M rows unless gathered
+    int A_rows;               // rows of A (gathered: S)
     int N;                    // output columns
     int K;                    // reduction length (multiple of 64)
     int topk;                 // k (token = flat route index / k)
@@ -92,77 +96,79 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams p) {
     if (expert < 0 || row0 >= row1) return;
     const int n0 = nt * BN;
     const int N = p.N, K = p.K;
-    const size_t b_off = (size_t)expert * (size_t)K * (size_t)N;
+    const uint32_t ldb = (uint32_t)N * 2u;  // bytes per B row
 
-    // ---- A loader: thread -> (row, chunk), row pointer fixed for the tile ----
-    const uint16_t *a_src[A_ITERS];
+    // ---- A: buffer over the rows this tile may touch ----
+    // gathered: the whole X; contiguous: rows [row0, row0 + BM) of A
+    const uint16_t *a_base = (MODE == kGateUp) ? p.A : p.A + (size_t)row0 * K;
+    const uint32_t a_bytes = (MODE == kGateUp) ? (uint32_t)((size_t)p.A_rows * K * 2)
+                                               : (uint32_t)((size_t)(row1 - row0) * K * 2);
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, a_bytes);
+    uint32_t a_voff[A_ITERS];
     int a_lds[A_ITERS];
 #pragma unroll
     for (int i = 0; i < A_ITERS; ++i) {
         const int idx = tid + 256 * i;
-        const int r = idx >> 3, c = idx & 7;
-        int slot = row0 + (r < BM ? r : 0);
+        const int r = (idx >> 3) < BM ? (idx >> 3) : 0;
+        const int c = idx & 7;
+        int slot = row0 + r;
         if (slot >= row1) slot = row1 - 1;  // rows past the expert's end load a valid row, never stored
-        long arow;
-        if (MODE == kGateUp) arow = p.slot_src[slot] / p.topk;
-        else arow = slot;
-        a_src[i] = p.A + arow * (long)K + c * 8;
+        const uint32_t arow = (MODE == kGateUp) ? (uint32_t)(p.slot_src[slot] / p.topk) : (uint32_t)(slot - row0);
+        a_voff[i] = arow * (uint32_t)K * 2u + (uint32_t)c * 16u;
         a_lds[i] = lds_off(r, c);
     }
-    // ---- B loader: thread -> 8x8 block (k rows kb*8.., n cols nb*8..) ----
-    const uint16_t *b_src[B_ITERS];
-    int b_lds_row[B_ITERS];
-    int b_kb[B_ITERS];
-    bool b_ok[B_ITERS];
+    // ---- B: thread -> 8x8 block (k rows kb*8.., n cols nb*8..) of one matrix ----
+    const size_t b_off = (size_t)expert * (size_t)K * (size_t)N;
+    const uint32_t b_bytes = (uint32_t)((size_t)K * N * 2);
+    const __amdgpu_buffer_rsrc_t b_rsrc0 = make_rsrc(p.B0 + b_off, b_bytes);
+    const __amdgpu_buffer_rsrc_t b_rsrc1 = make_rsrc((NB == 2 ? p.B1 : p.B0) + b_off, b_bytes);
+    static_assert(BN % 64 == 0, "a wave's 64 B blocks must come from one matrix");
+    uint32_t b_voff[B_ITERS];
+    int b_lds_row[B_ITERS], b_kb[B_ITERS];
+    __amdgpu_buffer_rsrc_t b_rsrc[B_ITERS];
 #pragma unroll
     for (int i = 0; i < B_ITERS; ++i) {
-        const int blk = tid + 256 * i;
+        const int blk = (tid + 256 * i) % B_BLOCKS;
         const int kb = blk & 7, nb = blk >> 3;
-        const int which = nb / (BN / 8);
+        // which matrix (W1 or W3) is uniform across the wave: make that explicit
+        const int which = __builtin_amdgcn_readfirstlane(nb / (BN / 8));
         const int ncol = (nb % (BN / 8)) * 8;
-        const uint16_t *base = (NB == 2 && which == 1) ? p.B1 : p.B0;
-        b_ok[i] = (blk < B_BLOCKS) && (n0 + ncol < N);
-        b_src[i] = base + b_off + (size_t)(kb * 8) * N + (b_ok[i] ? n0 + ncol : 0);
-        b_lds_row[i] = which * BN + ncol;  // first LDS row (n) of the block, within the B region
+        const int gcol = min(n0 + ncol, N - 8);  // columns past N only feed unstored outputs
+        b_rsrc[i] = (NB == 2 && which == 1) ? b_rsrc1 : b_rsrc0;
+        b_voff[i] = (uint32_t)(kb * 8) * ldb + (uint32_t)gcol * 2u;
+        b_lds_row[i] = which * BN + ncol;
         b_kb[i] = kb;
     }
 
     uint4 ra[A_ITERS];
     uint4 rb[B_ITERS][8];
+    constexpr bool A_FULL = (A_CHUNKS % 256) == 0;
+    constexpr bool B_FULL = (B_BLOCKS % 256) == 0;
 
-    auto load_global = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i)
-            if (A_CHUNKS % 256 == 0 || tid + 256 * i < A_CHUNKS)
-                ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + kt * BK);
-#pragma unroll
-        for (int i = 0; i < B_ITERS; ++i) {
-            const uint16_t *src = b_src[i] + (size_t)kt * BK * N;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                if (b_ok[i]) rb[i][r] = *reinterpret_cast<const uint4 *>(src + (size_t)r * N);
-                else rb[i][r] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto store_lds = [&](int stage) {
-        char *sa = smem + stage * STAGE;
-        char *sb = sa + A_BYTES;
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i)
-            if (A_CHUNKS % 256 == 0 || tid + 256 * i < A_CHUNKS)
-                *reinterpret_cast<uint4 *>(sa + a_lds[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_ITERS; ++i) {
-            if (B_BLOCKS % 256 == 0 || tid + 256 * i < B_BLOCKS) {
-                uint4 t[8];
-                transpose8x8(rb[i], t);
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    *reinterpret_cast<uint4 *>(sb + lds_off(b_lds_row[i] + c, b_kb[i])) = t[c];
-            }
-        }
-    };
+#define SMOE_LOAD_GLOBAL(KT)                                                                      \
+    {                                                                                            \
+        const uint32_t a_soff = (uint32_t)(KT) * (BK * 2);                                       \
+        _Pragma("unroll") for (int i = 0; i < A_ITERS; ++i) if (A_FULL || tid + 256 * i < A_CHUNKS) \
+            ra[i] = buf_load16(a_rsrc, a_voff[i], a_soff);                                       \
+        const uint32_t b_soff = (uint32_t)(KT) * BK * ldb;                                       \
+        _Pragma("unroll") for (int i = 0; i < B_ITERS; ++i) if (B_FULL || tid + 256 * i < B_BLOCKS) { \
+            _Pragma("unroll") for (int r = 0; r < 8; ++r)                                        \
+                rb[i][r] = buf_load16(b_rsrc[i], b_voff[i] + r * ldb, b_soff); \
+        }                                                                                        \
+    }
+#define SMOE_STORE_LDS(STG)                                                                       \
+    {                                                                                            \
+        char *sa = smem + (STG) * STAGE;                                                         \
+        char *sb = sa + A_BYTES;                                                                 \
+        _Pragma("unroll") for (int i = 0; i < A_ITERS; ++i) if (A_FULL || tid + 256 * i < A_CHUNKS) \
+            *reinterpret_cast<uint4 *>(sa + a_lds[i]) = ra[i];                                   \
+        _Pragma("unroll") for (int i = 0; i < B_ITERS; ++i) if (B_FULL || tid + 256 * i < B_BLOCKS) { \
+            uint4 t[8];                                                                          \
+            transpose8x8(rb[i], t);                                                              \
+            _Pragma("unroll") for (int c = 0; c < 8; ++c)                                        \
+                *reinterpret_cast<uint4 *>(sb + lds_off(b_lds_row[i] + c, b_kb[i])) = t[c];      \
+        }                                                                                        \
+    }
 
     f32x4 acc[NB][MT][NT];
 #pragma unroll
@@ -173,15 +179,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams p) {
             for (int j = 0; j < NT; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int KT = K / BK;
-    load_global(0);
-    store_lds(0);
+    SMOE_LOAD_GLOBAL(0);
+    SMOE_STORE_LDS(0);
     __syncthreads();
 
     const int frag_row = lane & 15;
     const int frag_chunk = lane >> 4;
     for (int kt = 0; kt < KT; ++kt) {
         const int stage = kt & 1;
-        if (kt + 1 < KT) load_global(kt + 1);
+        const bool more = kt + 1 < KT;
+        if (more) SMOE_LOAD_GLOBAL(kt + 1);
         const char *sa = smem + stage * STAGE;
         const char *sb = sa + A_BYTES;
 #pragma unroll
@@ -204,9 +211,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams p) {
 #pragma unroll
                     for (int j = 0; j < NT; ++j) acc[b][i][j] = mfma_16x16x32(af[i], bfr[b][j], acc[b][i][j]);
         }
-        if (kt + 1 < KT) store_lds(stage ^ 1);
+        if (more) SMOE_STORE_LDS(stage ^ 1);
         __syncthreads();
     }
+#undef SMOE_LOAD_GLOBAL
+#undef SMOE_STORE_LDS
 
     // ---- epilogue ----
     const int col_in_tile = lane & 15;

@@ -1,0 +1,337 @@
+// Ping-pong grouped, gathered bf16 GEMM for gfx950 (MFMA 16x16x32).
+//
+// Contract as grouped_gemm_kernel (gemm.hpp). One workgroup of 8 waves (two
+// per SIMD) computes a BM x BN tile of one expert with one of the three
+// epilogues (fused SwiGLU gate+up, router-weighted scatter-add, fp32 store).
+//
+// Operand path: HBM -> LDS by LDS DMA (buffer_load ... lds), A read back as
+// K-contiguous ds_read_b128 operands, B (weights, N-contiguous as stored)
+// read back with ds_read_b64_tr_b16 transposing reads. Within a 16-lane
+// group that instruction gives lane i element (i % 4) of the 8-byte piece
+// addressed by lane 4 r + i / 4 (r = 0..3), so lane q of group g addresses
+// row k = 8 g + 4 h + q / 4, columns 4 (q % 4) .. + 3 of its 16-column
+// fragment and reads h = 0, 1 deliver K = 8 g .. 8 g + 7, the A operand's
+// K order.
+//
+// Schedule (k-steps of BK = 32 or 64): the waves form two groups of four (one wave
+// of each per SIMD), running the same sequence "read fragments of step k
+// from LDS | barrier | MFMAs of step k | barrier" one barrier phase apart,
+// so on every SIMD one wave feeds the matrix core while the other reads LDS.
+// The LDS holds a ring of STAGES steps. At the start of its read phase for
+// step k, group 0 issues the DMA of step k + STAGES - 1 into the slot of
+// step k - 1 (both groups finished reading it one phase earlier), so
+// STAGES - 1 steps of operands are in flight per CU; at the end of its MFMA
+// phase it waits until step k + 1 has landed, before the barrier that opens
+// step k + 1 to readers. The DMA is plain assembly with explicit vmcnt
+// bookkeeping because the compiler would drain every DMA before each LDS
+// read (it cannot prove the ring slots disjoint).
+#pragma once
+
+#include "gemm.hpp"
+
+namespace smoe {
+
+typedef short pp_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void pp_lds_void;
+typedef __attribute__((address_space(3))) pp_s16x4 pp_lds_s16x4;
+
+typedef int pp_i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (CDNA word 3: 32-bit data, no swizzle) in SGPRs;
+// loads at offsets >= bytes return zero.
+__device__ __forceinline__ pp_i32x4 pp_desc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    pp_i32x4 d;
+    d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    d[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    d[3] = 0x00020000;
+    return d;
+}
+
+// LDS DMA of one wave instruction: 64 lanes x 16 bytes into LDS
+// [lds, lds + 1024). Written as assembly so that the compiler does not drain
+// it before every later LDS read (it cannot prove the stages disjoint);
+// completion is waited for explicitly with s_waitcnt vmcnt. The instruction
+// writes no VGPR, so nothing can be overwritten while it is in flight.
+__device__ __forceinline__ void pp_dma16(const pp_i32x4 &desc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(desc), "s"(soff), "{m0}"(lds)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint2 pp_tr(const char *p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((pp_lds_s16x4 *)(p)));
+}
+
+// Barrier that the compiler may move neither memory accesses nor other
+// instructions across.
+__device__ __forceinline__ void pp_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int N>
+__device__ __forceinline__ void pp_wait_dma() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// A tile rows are BK bf16 = CH chunks of 16 B (CH = 4 or 8). The chunk index
+// is XORed with a function of the row that keeps the 16 rows one
+// ds_read_b128 touches (one chunk each) in distinct banks, for LDS that
+// serves 128 or 256 bytes per cycle.
+template <int CH>
+__device__ __forceinline__ int pp_a_swz(int r) {
+    return (CH == 8) ? (((r >> 1) ^ ((r & 1) << 2)) & 7) : ((((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1));
+}
+// B tile rows: BN bf16 in 32-byte segments (16 columns); segment XOR by k.
+template <int SEGS>
+__device__ __forceinline__ int pp_b_swz(int k) {
+    return (SEGS >= 8) ? ((k & 3) | (((k >> 3) & 1) << 2)) : (k & (SEGS - 1));
+}
+
+template <int BM, int BN, int MODE, int BK, int STAGES>
+__global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p) {
+    constexpr int NB = (MODE == kGateUp) ? 2 : 1;
+    static_assert(BK == 32 || BK == 64, "K step");
+    constexpr int KK = BK / 32;                     // MFMA K sub-steps per step
+    constexpr int CH = BK / 8;                      // 16-byte chunks per A row
+    constexpr int WM = 2, WN = 4;                   // 8 waves: 2 row blocks x 4 column blocks
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int MT = WTM / 16, NT = WTN / 16;
+    static_assert(MT >= 1 && NT >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be 16-aligned");
+    static_assert(BN % 64 == 0 && BN <= 512, "B rows are 128..1024 bytes");
+    constexpr int A_ROW = BK * 2;                   // 64 or 128 B
+    constexpr int A_BYTES = BM * A_ROW;
+    constexpr int B_ROW = BN * 2;
+    constexpr int B_BYTES = BK * B_ROW;
+    constexpr int STAGE = A_BYTES + NB * B_BYTES;
+    constexpr int A_INSTR = A_BYTES / 1024;
+    constexpr int A_ROWS_PER_INSTR = 1024 / A_ROW;
+    constexpr int B_INSTR_PER_MAT = B_BYTES / 1024;
+    constexpr int B_INSTR = NB * B_INSTR_PER_MAT;
+    constexpr int B_ROWS_PER_INSTR = 1024 / B_ROW;
+    constexpr int B_LANES_PER_ROW = B_ROW / 16;
+    constexpr int SEGS = BN / 16;
+    static_assert(A_INSTR % 4 == 0 && B_INSTR % 4 == 0, "DMA split evenly over the 4 loading waves");
+    constexpr int A_PER_WAVE = A_INSTR / 4;
+    constexpr int B_PER_WAVE = B_INSTR / 4;
+    constexpr int DMA_PER_WAVE = A_PER_WAVE + B_PER_WAVE;
+    static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS ring");
+    static_assert(DMA_PER_WAVE * (STAGES - 2) < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int group = wave >> 2;                    // waves w and w + 4 share a SIMD
+    const int wl = wave & 3;                        // index within the group
+    const int wm = wave & 1, wn = wave >> 1;        // group 0: column blocks 0, 1; group 1: 2, 3
+
+    // ---- tile decode: XCD-contiguous logical id, grouped M-major order ----
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_group = p.group_m * p.n_ntiles;
+    const int grp = L / per_group;
+    const int within = L - grp * per_group;
+    const int m_first = grp * p.group_m;
+    const int gm = min(p.group_m, p.n_mtiles - m_first);
+    const int nt = within / gm;
+    const int mt = m_first + (within - nt * gm);
+
+    int expert, row0, row1;
+    if (MODE == kLogits) {
+        expert = 0;
+        row0 = mt * BM;
+        row1 = min(p.M, row0 + BM);
+    } else {
+        const int4 t = p.tiles[mt];
+        expert = t.x;
+        row0 = t.y;
+        row1 = t.z;
+    }
+    if (expert < 0 || row0 >= row1) return;
+    const int n0 = nt * BN;
+    const int N = p.N, K = p.K;
+    const uint32_t ldb = (uint32_t)N * 2u;
+
+    // ---- DMA sources (group 0 only) ----
+    const uint16_t *a_base = (MODE == kGateUp) ? p.A : p.A + (size_t)row0 * K;
+    const uint32_t a_bytes = (MODE == kGateUp) ? (uint32_t)((size_t)p.A_rows * K * 2)
+                                               : (uint32_t)((size_t)(row1 - row0) * K * 2);
+    const pp_i32x4 a_rsrc = pp_desc(a_base, a_bytes);
+    const size_t b_off = (size_t)expert * (size_t)K * (size_t)N;
+    const uint32_t b_bytes = (uint32_t)((size_t)K * N * 2);
+    const pp_i32x4 b_rsrc0 = pp_desc(p.B0 + b_off, b_bytes);
+    const pp_i32x4 b_rsrc1 = pp_desc((NB == 2 ? p.B1 : p.B0) + b_off, b_bytes);
+    const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+    uint32_t a_voff[A_PER_WAVE], b_voff[B_PER_WAVE];
+    if (group == 0) {
+#pragma unroll
+        for (int i = 0; i < A_PER_WAVE; ++i) {
+            const int j = wl + 4 * i;               // instruction: A_ROWS_PER_INSTR rows
+            const int r = A_ROWS_PER_INSTR * j + lane / CH;
+            const int c = (lane % CH) ^ pp_a_swz<CH>(r);
+            int slot = row0 + r;
+            if (slot >= row1) slot = row1 - 1;      // never stored; keeps gathered reads in range
+            const uint32_t arow =
+                (MODE == kGateUp) ? (uint32_t)(p.slot_src[slot] / p.topk) : (uint32_t)(slot - row0);
+            a_voff[i] = arow * (uint32_t)K * 2u + (uint32_t)c * 16u;
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER_WAVE; ++i) {
+            const int j = wl + 4 * i;
+            const int jj = j % B_INSTR_PER_MAT;
+            const int k = jj * B_ROWS_PER_INSTR + lane / B_LANES_PER_ROW;
+            const int pos = lane % B_LANES_PER_ROW;
+            const int seg = (pos >> 1) ^ pp_b_swz<SEGS>(k);
+            const int col = min(n0 + seg * 16 + (pos & 1) * 8, N - 8);  // columns past N feed unstored outputs
+            b_voff[i] = (uint32_t)k * ldb + (uint32_t)col * 2u;
+        }
+    }
+
+#define SMOE_PP_ISSUE(KT)                                                                          \
+    {                                                                                              \
+        const uint32_t sbase = smem_addr + ((KT) % STAGES) * STAGE;                                \
+        const uint32_t a_soff = (uint32_t)(KT) * (BK * 2);                                         \
+        _Pragma("unroll") for (int i = 0; i < A_PER_WAVE; ++i)                                     \
+            pp_dma16(a_rsrc, sbase + (wl + 4 * i) * 1024, a_voff[i], a_soff);                      \
+        const uint32_t b_soff = (uint32_t)(KT) * BK * ldb;                                         \
+        _Pragma("unroll") for (int i = 0; i < B_PER_WAVE; ++i) {                                   \
+            const int j = wl + 4 * i;                                                              \
+            pp_dma16((j / B_INSTR_PER_MAT) == 1 ? b_rsrc1 : b_rsrc0, sbase + A_BYTES + j * 1024,    \
+                     b_voff[i], b_soff);                                                           \
+        }                                                                                          \
+    }
+
+    // ---- fragment read offsets within a stage ----
+    const int fr = lane & 15, fg = lane >> 4;
+    int a_rd[KK][MT];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int row = wm * WTM + i * 16 + fr;
+            a_rd[kk][i] = row * A_ROW + (((kk * 4 + fg) ^ pp_a_swz<CH>(row)) << 4);
+        }
+    int b_rd[KK][NT][2];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = kk * 32 + 8 * fg + 4 * h + (fr >> 2);
+                const int n = wn * WTN + j * 16 + 4 * (fr & 3);
+                b_rd[kk][j][h] = A_BYTES + k * B_ROW + (((n >> 4) ^ pp_b_swz<SEGS>(k)) << 5) + (n & 15) * 2;
+            }
+
+    f32x4 acc[NB][MT][NT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = K / BK;
+    if (group == 0) {
+#pragma unroll
+        for (int st = 0; st < STAGES - 1; ++st)
+            if (st < KT) SMOE_PP_ISSUE(st);
+        if (KT >= STAGES - 1) pp_wait_dma<DMA_PER_WAVE * (STAGES - 2)>();  // step 0 landed
+        else pp_wait_dma<0>();
+    }
+    pp_barrier();
+    if (group == 1) pp_barrier();  // group 1 runs one phase behind
+
+    for (int kt = 0; kt < KT; ++kt) {
+        // ---- read phase: refill the slot of step kt-1, then read step kt ----
+        if (group == 0 && kt + STAGES - 1 < KT) SMOE_PP_ISSUE(kt + STAGES - 1);
+        const char *s = smem + (kt % STAGES) * STAGE;
+        uint4 af[KK][MT];
+        uint4 bf[KK][NB][NT];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i) af[kk][i] = *reinterpret_cast<const uint4 *>(s + a_rd[kk][i]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const uint2 lo = pp_tr(s + b * B_BYTES + b_rd[kk][j][0]);
+                    const uint2 hi = pp_tr(s + b * B_BYTES + b_rd[kk][j][1]);
+                    bf[kk][b][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+        }
+        // reads complete before the barrier: after it the slot may be refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        pp_barrier();
+        // ---- MFMA phase ----
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        acc[b][i][j] = mfma_16x16x32(af[kk][i], bf[kk][b][j], acc[b][i][j]);
+        __builtin_amdgcn_s_setprio(0);
+        if (group == 0) {  // step kt+1 must have landed before the barrier that opens it
+            if (kt + STAGES - 1 < KT) pp_wait_dma<DMA_PER_WAVE * (STAGES - 2)>();
+            else pp_wait_dma<0>();
+        }
+        pp_barrier();
+    }
+    if (group == 0) pp_barrier();
+#undef SMOE_PP_ISSUE
+
+    // ---- epilogue (C layout: lane holds column lane % 16, rows 4 (lane / 16) + r) ----
+    const int col_in_tile = lane & 15;
+    const int row_grp = (lane >> 4) * 4;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = wm * WTM + i * 16 + row_grp + r;
+            const int slot = row0 + row;
+            if (slot >= row1) continue;
+            if (MODE == kGateUp) {
+                uint16_t *h = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) {
+                        const float g = acc[0][i][j][r], u = acc[1][i][j][r];
+                        const float sg = g / (1.0f + __expf(-g));
+                        h[col] = f32_to_bf16_bits(sg * u);
+                    }
+                }
+            } else if (MODE == kDown) {
+                const int f = p.slot_src[slot];
+                const int tok = f / p.topk;
+                const float w = p.gate[f];
+                float *accp = reinterpret_cast<float *>(p.C) + (size_t)tok * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) atomicAdd(accp + col, w * acc[0][i][j][r]);
+                }
+            } else {
+                float *out = reinterpret_cast<float *>(p.C) + (size_t)slot * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) out[col] = acc[0][i][j][r];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace smoe

@@ -87,6 +87,7 @@ static void launch_logits(const uint16_t *x, const uint16_t *w_gate, int S, int 
     p.B0 = w_gate;
     p.C = logits;
     p.M = S;
+    p.A_rows = S;
     p.N = E;
     p.K = D;
     p.topk = 1;
