@@ -26,8 +26,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "MoE-layer fwd tokens/s + % bf16 MFMA peak (Mixtral-shape, S=4096, 1 GPU)"
-KERNEL_SOURCES = ["sparse_mixture_experts_gemv_amd/csrc/gemm.hpp", "sparse_mixture_experts_gemv_amd/csrc/common.hpp",
-                  "sparse_mixture_experts_gemv_amd/csrc/ffn.hip"]
+KERNEL_SOURCES = ["sparse_mixture_experts_gemv_amd/csrc/gemm.hpp", "sparse_mixture_experts_gemv_amd/csrc/gemm_pp.hpp",
+                  "sparse_mixture_experts_gemv_amd/csrc/common.hpp", "sparse_mixture_experts_gemv_amd/csrc/ffn.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--S", type=int, default=None, help="token count (default: the configuration's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run three device-to-device copies of BYTES (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -117,6 +119,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings scale
+        # the same counters of the MoE kernels to bytes
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "launches": 3}))
+        return
     cfg = wl.CONFIGS[args.config]
     if args.S:
         cfg = cfg.with_S(args.S)

@@ -23,12 +23,20 @@
 namespace smoe {
 
 // One thread per expert: ceil(rows / bm) tiles each, exclusive scan over the
-// experts, then every expert writes its (expert, row_begin, row_end) entries.
-// Two tile heights are handled in one launch (one per GEMM); entries past the
-// real tile count are marked empty (expert = -1).
-__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restrict__ offsets, int E, int N, int bm0,
-                                                          int n0, int4 *__restrict__ tiles0, int bm1, int n1,
-                                                          int4 *__restrict__ tiles1) {
+// experts, then every expert writes its (expert, row_begin, row_end) entries
+// and the block order of its tiles: blocks [T_e * nt_n, (T_e + c_e) * nt_n)
+// hold expert e (T_e its first tile, c_e its tile count, nt_n the N tiles),
+// N tile major, the expert's c_e M tiles minor. Two GEMMs (tile heights) are
+// handled in one launch. Entries past the real tile count are marked empty
+// (expert = -1, order = 0xffff).
+struct TileTableArgs {
+    int bm[2], n_mtiles[2], n_ntiles[2];
+    int4 *tiles[2];
+    uint32_t *order[2];
+};
+
+__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restrict__ offsets, int E, int N,
+                                                          const TileTableArgs a) {
     __shared__ int s_wave[2][16];
     const int e = threadIdx.x;
     const int lane = e & 63, w = e >> 6;
@@ -37,13 +45,10 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restr
         off = min(max(offsets[e], 0), N);
         end = min(max(offsets[e + 1], off), N);
     }
-    const int bms[2] = {bm0, bm1};
-    const int ns[2] = {n0, n1};
-    int4 *const tabs[2] = {tiles0, tiles1};
     int t[2], x[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        t[q] = (e < E) ? (end - off + bms[q] - 1) / bms[q] : 0;
+        t[q] = (e < E) ? (end - off + a.bm[q] - 1) / a.bm[q] : 0;
         x[q] = t[q];
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -55,16 +60,22 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restr
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        if (tabs[q] == nullptr) continue;
         int base = 0, total = 0;
         for (int i = 0; i < 16; ++i) {
             if (i < w) base += s_wave[q][i];
             total += s_wave[q][i];
         }
         base += x[q] - t[q];
-        for (int i = 0; i < t[q] && base + i < ns[q]; ++i)
-            tabs[q][base + i] = make_int4(e, off + i * bms[q], min(off + (i + 1) * bms[q], end), 0);
-        for (int j = total + threadIdx.x; j < ns[q]; j += 1024) tabs[q][j] = make_int4(-1, 0, 0, 0);
+        const int nm = a.n_mtiles[q], nn = a.n_ntiles[q];
+        const int cnt = min(t[q], max(nm - base, 0));
+        for (int i = 0; i < cnt; ++i)
+            a.tiles[q][base + i] = make_int4(e, off + i * a.bm[q], min(off + (i + 1) * a.bm[q], end), 0);
+        for (int n = 0; n < nn; ++n)
+            for (int i = 0; i < cnt; ++i)
+                a.order[q][(size_t)base * nn + (size_t)n * cnt + i] = (uint32_t)(base + i) | ((uint32_t)n << 16);
+        const int valid = min(total, nm);
+        for (int j = valid + threadIdx.x; j < nm; j += 1024) a.tiles[q][j] = make_int4(-1, 0, 0, 0);
+        for (size_t j = (size_t)valid * nn + threadIdx.x; j < (size_t)nm * nn; j += 1024) a.order[q][j] = 0xffffu;
     }
 }
 
@@ -112,11 +123,19 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
     pick_gemm(avg, pl.kind_down, pl.bm_down);
     pl.n_mtiles_up = tiles_upper_bound(N, E, pl.bm_up);
     pl.n_mtiles_down = tiles_upper_bound(N, E, pl.bm_down);
+    pl.bn_up = (pl.kind_up == kKindPP) ? 128 : 128;
+    pl.bn_down = (pl.kind_down == kKindPP) ? 256 : 128;
+    pl.n_ntiles_up = (int)((F + pl.bn_up - 1) / pl.bn_up);
+    pl.n_ntiles_down = (int)((D + pl.bn_down - 1) / pl.bn_down);
     size_t off = 0;
     pl.tiles_up_off = off;
     off += align_up((size_t)std::max(pl.n_mtiles_up, 1) * sizeof(int4));
     pl.tiles_down_off = off;
     off += align_up((size_t)std::max(pl.n_mtiles_down, 1) * sizeof(int4));
+    pl.order_up_off = off;
+    off += align_up((size_t)std::max(pl.n_mtiles_up, 1) * pl.n_ntiles_up * sizeof(uint32_t));
+    pl.order_down_off = off;
+    off += align_up((size_t)std::max(pl.n_mtiles_down, 1) * pl.n_ntiles_down * sizeof(uint32_t));
     pl.h_off = off;
     off += align_up((size_t)N * (size_t)F * 2);
     pl.acc_off = off;
@@ -133,7 +152,7 @@ static int grid_for(size_t n, int per_block) {
 template <int BM, int BN, int WM, int WN, int MODE>
 static void launch_reg(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
-    p.n_ntiles = (p.N + BN - 1) / BN;
+    p.n_ntiles = (p.N + BN - 1) / BN;  // equals the plan's count the order table was built for
     const int blocks = p.n_mtiles * p.n_ntiles;
     if (blocks == 0) return;
     grouped_gemm_kernel<BM, BN, WM, WN, MODE><<<blocks, 256, 0, stream>>>(p);
@@ -183,9 +202,21 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     const int N = S * k;
     const size_t n4 = (size_t)S * D / 4;
 
+    uint32_t *order_up = reinterpret_cast<uint32_t *>(ws + pl.order_up_off);
+    uint32_t *order_down = reinterpret_cast<uint32_t *>(ws + pl.order_down_off);
+    TileTableArgs ta;
+    ta.bm[0] = pl.bm_up;
+    ta.bm[1] = pl.bm_down;
+    ta.n_mtiles[0] = pl.n_mtiles_up;
+    ta.n_mtiles[1] = pl.n_mtiles_down;
+    ta.n_ntiles[0] = pl.n_ntiles_up;
+    ta.n_ntiles[1] = pl.n_ntiles_down;
+    ta.tiles[0] = tiles_up;
+    ta.tiles[1] = tiles_down;
+    ta.order[0] = order_up;
+    ta.order[1] = order_down;
     prof_begin(stream, kKTileTable);
-    tile_table_kernel<<<1, 1024, 0, stream>>>(expert_offsets, E, N, pl.bm_up, pl.n_mtiles_up, tiles_up, pl.bm_down,
-                                              pl.n_mtiles_down, tiles_down);
+    tile_table_kernel<<<1, 1024, 0, stream>>>(expert_offsets, E, N, ta);
     prof_end(stream, kKTileTable);
     prof_begin(stream, kKAccZero);
     acc_zero_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<float4 *>(acc), n4);
@@ -200,6 +231,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
 
     // gate + up: A = gathered token rows of x, K = D, N = F
     p.tiles = tiles_up;
+    p.order = order_up;
     p.n_mtiles = pl.n_mtiles_up;
     p.A = x;
     p.B0 = w1;
@@ -212,6 +244,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
 
     // down + scatter-add: A = h (slot order), K = F, N = D
     p.tiles = tiles_down;
+    p.order = order_down;
     p.n_mtiles = pl.n_mtiles_down;
     p.A = h;
     p.B0 = w2;

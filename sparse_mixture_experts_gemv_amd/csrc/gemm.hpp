@@ -38,6 +38,7 @@ struct GemmParams {
     const int32_t *slot_src;  // [S*k] slot -> flat route index
     const float *gate;        // [S*k] router weights (kDown)
     const int4 *tiles;        // [n_mtiles] (expert, row_begin, row_end, -) ; expert < 0 = empty
+    const uint32_t *order;    // [n_mtiles * n_ntiles] logical block -> mt | nt << 16 (nullptr: grouped order)
     void *C;                  // h bf16 [S*k, N] / acc fp32 [S, N] / logits fp32 [S, N]
     int M;                    // rows (kLogits: S); A has M rows unless gathered
     int A_rows;               // rows of A (gathered: S)
@@ -48,6 +49,29 @@ struct GemmParams {
     int n_ntiles;
     int group_m;              // M tiles per tile group (L2 reuse order)
 };
+
+// Block -> (M tile, N tile). Logical ids are XCD-contiguous (xcd_remap). With
+// an order table (built next to the tile table) the logical order is
+// expert-major, then N tile, then the expert's M tiles: the blocks that share
+// one expert's weight panel run back to back on one XCD. Without it, M tiles
+// are taken in groups of group_m per N tile. Returns false for an empty slot.
+__device__ __forceinline__ bool decode_tile(const GemmParams &p, int &mt, int &nt) {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    if (p.order != nullptr) {
+        const uint32_t v = p.order[L];
+        mt = (int)(v & 0xffffu);
+        nt = (int)(v >> 16);
+        return mt < p.n_mtiles;
+    }
+    const int per_group = p.group_m * p.n_ntiles;
+    const int grp = L / per_group;
+    const int within = L - grp * per_group;
+    const int m_first = grp * p.group_m;
+    const int gm = min(p.group_m, p.n_mtiles - m_first);
+    nt = within / gm;
+    mt = m_first + (within - nt * gm);
+    return true;
+}
 
 template <int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams p) {
@@ -72,15 +96,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams p) {
     const int wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    // ---- tile decode: XCD-contiguous logical id, grouped M-major order ----
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int per_group = p.group_m * p.n_ntiles;
-    const int grp = L / per_group;
-    const int within = L - grp * per_group;
-    const int m_first = grp * p.group_m;
-    const int gm = min(p.group_m, p.n_mtiles - m_first);
-    const int nt = within / gm;
-    const int mt = m_first + (within - nt * gm);
+    int mt, nt;
+    if (!decode_tile(p, mt, nt)) return;
 
     int expert, row0, row1;
     if (MODE == kLogits) {

@@ -132,15 +132,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p
     const int wl = wave & 3;                        // index within the group
     const int wm = wave & 1, wn = wave >> 1;        // group 0: column blocks 0, 1; group 1: 2, 3
 
-    // ---- tile decode: XCD-contiguous logical id, grouped M-major order ----
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int per_group = p.group_m * p.n_ntiles;
-    const int grp = L / per_group;
-    const int within = L - grp * per_group;
-    const int m_first = grp * p.group_m;
-    const int gm = min(p.group_m, p.n_mtiles - m_first);
-    const int nt = within / gm;
-    const int mt = m_first + (within - nt * gm);
+    int mt, nt;
+    if (!decode_tile(p, mt, nt)) return;
 
     int expert, row0, row1;
     if (MODE == kLogits) {

@@ -26,8 +26,10 @@ hipError_t launch_sparse_map(const int32_t *ids, int N, int E, int32_t *expert_c
 struct FfnPlan {
     int kind_up, bm_up;        // gate+up GEMM: kernel kind and rows per M tile
     int kind_down, bm_down;    // down GEMM
+    int bn_up, bn_down;        // columns per N tile
     int n_mtiles_up, n_mtiles_down;  // upper bounds on M tiles over all experts
-    size_t tiles_up_off, tiles_down_off, h_off, acc_off, ws_bytes;
+    int n_ntiles_up, n_ntiles_down;
+    size_t tiles_up_off, tiles_down_off, order_up_off, order_down_off, h_off, acc_off, ws_bytes;
 };
 FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k);
 hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
