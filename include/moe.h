@@ -72,8 +72,9 @@ const char *moe_status_str(int status);
 int moe_version(void);
 
 /*
- * Workspace bytes moe_route_topk needs for these sizes (router logits in
- * fp32, [S, E]). Pure host function.
+ * Workspace bytes moe_route_topk needs for these sizes (partial router
+ * logits in fp32, [splits, S, E], for E > 16; zero for E <= 16). Pure host
+ * function.
  */
 size_t moe_route_workspace_bytes(int32_t S, int32_t E);
 
@@ -81,7 +82,9 @@ size_t moe_route_workspace_bytes(int32_t S, int32_t E);
  * Router (ScatterMoE Guide, section "1. The Dynamic Routing Imbalance
  * Dilemma", equation H(X); the page's FFN block computes the same thing as
  * softmax, top-k, renormalise).
- *   logits[s, e] = sum_d x[s, d] * w_gate[d, e]      (bf16 in, fp32 sum)
+ *   logits[s, e] = sum_d x[s, d] * w_gate[d, e]      (bf16 in, fp32 sum;
+ *                  the order of the fp32 sum is fixed, so ids are
+ *                  reproducible run to run)
  *   topk_ids[s, 0..k-1]  = the k largest logits, descending; equal logits
  *                          rank the lower expert id first
  *   topk_weights[s, j]   = exp(l_j - l_0) / sum_j' exp(l_j' - l_0)  (fp32)
@@ -143,7 +146,8 @@ size_t moe_scatter_ffn_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t 
  * ids; out [S, D] bf16 (fully written; tokens with no route get zeros).
  * workspace >= moe_scatter_ffn_workspace_bytes(S, D, F, E, k).
  * Limits: D % 64 == 0, F % 64 == 0, E <= 1024, S*D < 2^30, D*F < 2^30
- * (32-bit buffer offsets; else UNSUPPORTED).
+ * (32-bit buffer offsets), D <= 2^19, F <= 2^19 and fewer than 2^20 - 1 row
+ * tiles (always true for S*k < 2^26): else UNSUPPORTED.
  */
 int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                         const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,

@@ -92,7 +92,9 @@ int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
     // 32-bit buffer offsets: x, each expert matrix and each tile's rows of h stay below 2 GiB
     if (N >= ((int64_t)1 << 31) || (int64_t)S * D >= ((int64_t)1 << 30) || (int64_t)D * F >= ((int64_t)1 << 30))
         return MOE_ERR_UNSUPPORTED;
-    if (workspace_bytes < smoe::ffn_plan(S, D, F, E, k).ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    const smoe::FfnPlan plan = smoe::ffn_plan(S, D, F, E, k);
+    if (!smoe::ffn_plan_fits(plan)) return MOE_ERR_UNSUPPORTED;
+    if (workspace_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
     return finish(smoe::launch_scatter_ffn(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, S, D, F, E, k, out,
                                            workspace, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -22,22 +22,25 @@
 
 namespace smoe {
 
-// One thread per expert: ceil(rows / bm) tiles each, exclusive scan over the
-// experts, then every expert writes its (expert, row_begin, row_end) entries
-// and the block order of its tiles: blocks [T_e * nt_n, (T_e + c_e) * nt_n)
-// hold expert e (T_e its first tile, c_e its tile count, nt_n the N tiles),
-// N tile major, the expert's c_e M tiles minor. Two GEMMs (tile heights) are
-// handled in one launch. Entries past the real tile count are marked empty
-// (expert = -1, order = 0xffff).
+// One thread per expert computes ceil(rows / bm) tiles, an exclusive scan
+// gives each expert its first tile T_e, and the expert writes its
+// (expert, row_begin, row_end) entries. The block order is then filled by all
+// threads: blocks [T_e * nn, (T_e + c_e) * nn) belong to expert e (c_e its
+// tile count, nn the N tiles), N tile major, the expert's M tiles minor; a
+// thread finds the expert of a block by binary search over T_e. Two GEMMs
+// (tile heights) are handled in one launch. Entries past the real tile count
+// are marked empty (expert = -1, order M field all ones).
 struct TileTableArgs {
     int bm[2], n_mtiles[2], n_ntiles[2];
     int4 *tiles[2];
     uint32_t *order[2];
+    int *valid[2];  // number of non-empty M tiles
 };
 
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restrict__ offsets, int E, int N,
                                                           const TileTableArgs a) {
     __shared__ int s_wave[2][16];
+    __shared__ int s_first[2][1025];  // T_e, with T_E = total
     const int e = threadIdx.x;
     const int lane = e & 63, w = e >> 6;
     int off = 0, end = 0;
@@ -66,16 +69,41 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restr
             total += s_wave[q][i];
         }
         base += x[q] - t[q];
-        const int nm = a.n_mtiles[q], nn = a.n_ntiles[q];
+        const int nm = a.n_mtiles[q];
+        const int valid = min(total, nm);
+        if (e < E) s_first[q][e] = min(base, valid);
+        if (e == 0) {
+            s_first[q][E] = valid;
+            *a.valid[q] = valid;
+        }
         const int cnt = min(t[q], max(nm - base, 0));
         for (int i = 0; i < cnt; ++i)
             a.tiles[q][base + i] = make_int4(e, off + i * a.bm[q], min(off + (i + 1) * a.bm[q], end), 0);
-        for (int n = 0; n < nn; ++n)
-            for (int i = 0; i < cnt; ++i)
-                a.order[q][(size_t)base * nn + (size_t)n * cnt + i] = (uint32_t)(base + i) | ((uint32_t)n << 16);
-        const int valid = min(total, nm);
         for (int j = valid + threadIdx.x; j < nm; j += 1024) a.tiles[q][j] = make_int4(-1, 0, 0, 0);
-        for (size_t j = (size_t)valid * nn + threadIdx.x; j < (size_t)nm * nn; j += 1024) a.order[q][j] = 0xffffu;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int nm = a.n_mtiles[q], nn = a.n_ntiles[q];
+        const int valid = s_first[q][E];
+        const size_t vblocks = (size_t)valid * nn;
+        for (size_t L = threadIdx.x; L < (size_t)nm * nn; L += 1024) {
+            uint32_t v = kOrderMtMask;
+            if (L < vblocks) {
+                // expert: the last e with T_e * nn <= L (experts with no tiles share T_e)
+                int lo = 0, hi = E - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if ((size_t)s_first[q][mid] * nn <= L) lo = mid;
+                    else hi = mid - 1;
+                }
+                const int first = s_first[q][lo];
+                const int cnt = s_first[q][lo + 1] - first;
+                const int idx = (int)(L - (size_t)first * nn);
+                v = (uint32_t)(first + idx % cnt) | ((uint32_t)(idx / cnt) << kOrderMtBits);
+            }
+            a.order[q][L] = v;
+        }
     }
 }
 
@@ -136,6 +164,8 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
     off += align_up((size_t)std::max(pl.n_mtiles_up, 1) * pl.n_ntiles_up * sizeof(uint32_t));
     pl.order_down_off = off;
     off += align_up((size_t)std::max(pl.n_mtiles_down, 1) * pl.n_ntiles_down * sizeof(uint32_t));
+    pl.counts_off = off;
+    off += align_up(2 * sizeof(int));
     pl.h_off = off;
     off += align_up((size_t)N * (size_t)F * 2);
     pl.acc_off = off;
@@ -167,6 +197,27 @@ static void launch_pp(const GemmParams &p0, hipStream_t stream) {
     grouped_gemm_pp_kernel<BM, BN, MODE, BK, STAGES><<<blocks, 512, 0, stream>>>(p);
 }
 
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Stream-K down GEMM: one persistent workgroup per CU (160 KB of LDS each).
+template <int BM, int BN, int BK, int STAGES>
+static void launch_pp_streamk(const GemmParams &p0, hipStream_t stream) {
+    GemmParams p = p0;
+    p.n_ntiles = (p.N + BN - 1) / BN;
+    if (p.n_mtiles * p.n_ntiles == 0) return;
+    grouped_gemm_pp_streamk_kernel<BM, BN, BK, STAGES><<<device_cus(), 512, 0, stream>>>(p);
+}
+
 template <int MODE>
 static void launch_gemm(int kind, int bm, const GemmParams &p, hipStream_t stream) {
     const int kid = MODE == kGateUp ? kKGateUp : kKDown;
@@ -176,7 +227,7 @@ static void launch_gemm(int kind, int bm, const GemmParams &p, hipStream_t strea
             if (bm == 256) launch_pp<256, 128, MODE, 64, 2>(p, stream);
             else launch_pp<128, 128, MODE, 32, 5>(p, stream);
         } else {
-            if (bm == 256) launch_pp<256, 256, MODE, 32, 5>(p, stream);
+            if (bm == 256) launch_pp_streamk<256, 256, 32, 5>(p, stream);
             else launch_pp<128, 256, MODE, 64, 3>(p, stream);
         }
     } else {
@@ -215,6 +266,9 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     ta.tiles[1] = tiles_down;
     ta.order[0] = order_up;
     ta.order[1] = order_down;
+    int *valid_counts = reinterpret_cast<int *>(ws + pl.counts_off);
+    ta.valid[0] = valid_counts;
+    ta.valid[1] = valid_counts + 1;
     prof_begin(stream, kKTileTable);
     tile_table_kernel<<<1, 1024, 0, stream>>>(expert_offsets, E, N, ta);
     prof_end(stream, kKTileTable);
@@ -245,6 +299,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     // down + scatter-add: A = h (slot order), K = F, N = D
     p.tiles = tiles_down;
     p.order = order_down;
+    p.valid_mtiles = valid_counts + 1;
     p.n_mtiles = pl.n_mtiles_down;
     p.A = h;
     p.B0 = w2;

@@ -26,6 +26,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace smoe {
 
@@ -39,6 +40,7 @@ struct GemmParams {
     const float *gate;        // [S*k] router weights (kDown)
     const int4 *tiles;        // [n_mtiles] (expert, row_begin, row_end, -) ; expert < 0 = empty
     const uint32_t *order;    // [n_mtiles * n_ntiles] logical block -> mt | nt << 16 (nullptr: grouped order)
+    const int *valid_mtiles;  // device count of non-empty M tiles (stream-K kernels)
     void *C;                  // h bf16 [S*k, N] / acc fp32 [S, N] / logits fp32 [S, N]
     int M;                    // rows (kLogits: S); A has M rows unless gathered
     int A_rows;               // rows of A (gathered: S)
@@ -59,8 +61,8 @@ __device__ __forceinline__ bool decode_tile(const GemmParams &p, int &mt, int &n
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     if (p.order != nullptr) {
         const uint32_t v = p.order[L];
-        mt = (int)(v & 0xffffu);
-        nt = (int)(v >> 16);
+        mt = (int)(v & kOrderMtMask);
+        nt = (int)(v >> kOrderMtBits);
         return mt < p.n_mtiles;
     }
     const int per_group = p.group_m * p.n_ntiles;

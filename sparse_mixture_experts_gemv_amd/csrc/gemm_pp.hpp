@@ -94,7 +94,17 @@ __device__ __forceinline__ int pp_b_swz(int k) {
 }
 
 template <int BM, int BN, int MODE, int BK, int STAGES>
-__global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p) {
+struct PPGeom {
+    static constexpr int NB = (MODE == kGateUp) ? 2 : 1;
+    static constexpr int STAGE = BM * BK * 2 + NB * BK * BN * 2;
+    static constexpr int SMEM = STAGES * STAGE;
+};
+
+// One tile (mt, nt), k-steps [k_begin, k_end) of BK, epilogue included. All
+// 512 threads of the workgroup call it together; on return every LDS read of
+// the ring has completed, so the caller may start another tile.
+template <int BM, int BN, int MODE, int BK, int STAGES>
+__device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt, int nt, int k_begin, int k_end) {
     constexpr int NB = (MODE == kGateUp) ? 2 : 1;
     static_assert(BK == 32 || BK == 64, "K step");
     constexpr int KK = BK / 32;                     // MFMA K sub-steps per step
@@ -123,17 +133,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p
     static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS ring");
     static_assert(DMA_PER_WAVE * (STAGES - 2) < 64, "vmcnt range");
 
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int group = wave >> 2;                    // waves w and w + 4 share a SIMD
     const int wl = wave & 3;                        // index within the group
     const int wm = wave & 1, wn = wave >> 1;        // group 0: column blocks 0, 1; group 1: 2, 3
-
-    int mt, nt;
-    if (!decode_tile(p, mt, nt)) return;
 
     int expert, row0, row1;
     if (MODE == kLogits) {
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p
 
 #define SMOE_PP_ISSUE(KT)                                                                          \
     {                                                                                              \
-        const uint32_t sbase = smem_addr + ((KT) % STAGES) * STAGE;                                \
+        const uint32_t sbase = smem_addr + SMOE_SLOT(KT) * STAGE;                                  \
         const uint32_t a_soff = (uint32_t)(KT) * (BK * 2);                                         \
         _Pragma("unroll") for (int i = 0; i < A_PER_WAVE; ++i)                                     \
             pp_dma16(a_rsrc, sbase + (wl + 4 * i) * 1024, a_voff[i], a_soff);                      \
@@ -230,21 +235,23 @@ __global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p
 #pragma unroll
             for (int j = 0; j < NT; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int KT = K / BK;
+    // k-steps [k_begin, k_end); ring slot of step kt is (kt - k_begin) % STAGES
+    const int KT = k_end;
+#define SMOE_SLOT(KT_) (((KT_) - k_begin) % STAGES)
     if (group == 0) {
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st)
-            if (st < KT) SMOE_PP_ISSUE(st);
-        if (KT >= STAGES - 1) pp_wait_dma<DMA_PER_WAVE * (STAGES - 2)>();  // step 0 landed
+            if (k_begin + st < KT) SMOE_PP_ISSUE(k_begin + st);
+        if (KT - k_begin >= STAGES - 1) pp_wait_dma<DMA_PER_WAVE * (STAGES - 2)>();  // first step landed
         else pp_wait_dma<0>();
     }
     pp_barrier();
     if (group == 1) pp_barrier();  // group 1 runs one phase behind
 
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = k_begin; kt < KT; ++kt) {
         // ---- read phase: refill the slot of step kt-1, then read step kt ----
         if (group == 0 && kt + STAGES - 1 < KT) SMOE_PP_ISSUE(kt + STAGES - 1);
-        const char *s = smem + (kt % STAGES) * STAGE;
+        const char *s = smem + SMOE_SLOT(kt) * STAGE;
         uint4 af[KK][MT];
         uint4 bf[KK][NB][NT];
 #pragma unroll
@@ -283,6 +290,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p
     }
     if (group == 0) pp_barrier();
 #undef SMOE_PP_ISSUE
+#undef SMOE_SLOT
 
     // ---- epilogue (C layout: lane holds column lane % 16, rows 4 (lane / 16) + r) ----
     const int col_in_tile = lane & 15;
@@ -324,6 +332,43 @@ __global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p
                 }
             }
         }
+    }
+}
+
+// One workgroup per output tile (full K).
+template <int BM, int BN, int MODE, int BK, int STAGES>
+__global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[PPGeom<BM, BN, MODE, BK, STAGES>::SMEM];
+    int mt, nt;
+    if (!decode_tile(p, mt, nt)) return;
+    pp_tile<BM, BN, MODE, BK, STAGES>(p, smem, mt, nt, 0, p.K / BK);
+}
+
+// Persistent stream-K form for the down GEMM, whose epilogue is an atomic
+// add (so a tile's K range may be split between workgroups: each part adds
+// its partial sum). The valid blocks of the order table, each cut into
+// K / BK k-steps, form one sequence of work units; workgroup b (in
+// XCD-contiguous order) takes units [U b / G, U (b + 1) / G) and runs every
+// (tile, k-range) piece of it. This removes the idle tail of the last wave of
+// tiles and evens out experts of different sizes.
+template <int BM, int BN, int BK, int STAGES>
+__global__ __launch_bounds__(512) void grouped_gemm_pp_streamk_kernel(const GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[PPGeom<BM, BN, kDown, BK, STAGES>::SMEM];
+    const int KT = p.K / BK;
+    const int valid_mtiles = min(*p.valid_mtiles, p.n_mtiles);
+    const long units = (long)valid_mtiles * p.n_ntiles * KT;
+    const int G = gridDim.x;
+    const int b = xcd_remap(blockIdx.x, G);
+    long u = units * b / G;
+    const long u_end = units * (b + 1) / G;
+    while (u < u_end) {
+        const int L = (int)(u / KT);
+        const int ks = (int)(u - (long)L * KT);
+        const int ke = (int)min((long)KT, (long)ks + (u_end - u));
+        const uint32_t v = p.order[L];
+        const int mt = (int)(v & kOrderMtMask), nt = (int)(v >> kOrderMtBits);
+        if (mt < p.n_mtiles) pp_tile<BM, BN, kDown, BK, STAGES>(p, smem, mt, nt, ks, ke);
+        u += ke - ks;
     }
 }
 

@@ -61,7 +61,7 @@ def test_route_validation(lib):
     assert r(FAKE, FAKE, 16, 96, 8, 2, FAKE, FAKE, FAKE, 1 << 20, None) == 2  # D % 64
     assert r(FAKE, FAKE, 16, 64, 12, 2, FAKE, FAKE, FAKE, 1 << 20, None) == 2  # E % 8
     assert r(FAKE, FAKE, 16, 64, 512, 2, FAKE, FAKE, FAKE, 1 << 20, None) == 2  # E > 256
-    assert r(FAKE, FAKE, 16, 64, 8, 2, FAKE, FAKE, FAKE, 16, None) == 3  # workspace
+    assert r(FAKE, FAKE, 16, 64, 64, 2, FAKE, FAKE, FAKE, 16, None) == 3  # workspace (E > 16 needs partial logits)
     assert r(None, None, 0, 64, 8, 2, None, None, None, 0, None) == 0  # S == 0: no-op
 
 
@@ -87,6 +87,7 @@ def test_ffn_validation(lib):
     assert f(*args(F=100)) == 2
     assert f(*args(E=2048, k=2)) == 2
     assert f(*args(ws=1024)) == 3
+    assert f(*args(S=1, D=1 << 20, F=64)) == 2  # 8192 column tiles of the down GEMM exceed the order table
     assert f(None, None, None, None, None, None, None, 0, 64, 128, 8, 2, None, None, 0, None) == 0
 
 
@@ -113,7 +114,8 @@ def test_workspace_has_no_token_replication(lib):
         base = S * k * F * 2 + S * 4096 * 4
         assert base <= d1 <= base + (1 << 20)
     # the router and map workspaces do not scale with D at all
-    assert lib.moe_route_workspace_bytes(4096, 256) == 4096 * 256 * 4
+    assert lib.moe_route_workspace_bytes(4096, 256) == 16 * 4096 * 256 * 4  # 16 K-splits of partial logits
+    assert lib.moe_route_workspace_bytes(4096, 8) == 0  # small-E router keeps logits in registers
     assert lib.moe_sparse_map_workspace_bytes(4096, 8, 256) < 1 << 20
 
 

@@ -51,19 +51,23 @@ def test_route_configs(oracle_lib, name):
 
 
 @pytest.mark.parametrize("S,D,E,k", [(1, 64, 8, 1), (37, 128, 16, 3), (300, 192, 64, 8), (129, 256, 256, 16),
-                                     (1000, 512, 96, 6), (65, 64, 8, 8)])
+                                     (1000, 512, 96, 6), (65, 64, 8, 8),
+                                     (50, 640, 16, 4), (19, 4096, 8, 2), (2053, 1152, 128, 4)])
 def test_route_shapes(oracle_lib, S, D, E, k):
     cfg = wl.MoEConfig("route", 90 + E, S, D, 64, E, k, None)
     check_route(oracle_lib, wl.gen_x(cfg).to(DEV), wl.gen_w_gate(cfg).to(DEV), k, f"shape {S}x{D}x{E}")
 
 
-def test_route_exact_ties(oracle_lib):
-    """Duplicated router columns tie exactly: the lower expert id ranks first."""
+@pytest.mark.parametrize("E", [8, 64])
+def test_route_exact_ties(oracle_lib, E):
+    """Duplicated router columns tie exactly: the lower expert id ranks first
+    (E = 8 runs the register router, E = 64 the MFMA logits + top-k pass)."""
     import sparse_mixture_experts_gemv_amd as smoe
-    cfg = wl.MoEConfig("ties", 77, 200, 128, 64, 8, 2, 0.05)
-    half = wl.gen_w_gate(cfg)[:, :4]
+    h = E // 2
+    cfg = wl.MoEConfig("ties", 77, 200, 128, 64, E, 2, 0.05)
+    half = wl.gen_w_gate(cfg)[:, :h]
     wg = torch.cat([half, half], dim=1).contiguous().to(DEV)
     ids, w = smoe.moe_route_topk(wl.gen_x(cfg).to(DEV), wg, 2)
     ids, w = ids.cpu().numpy(), w.cpu().numpy()
-    assert np.all(ids[:, 0] < 4) and np.all(ids[:, 1] == ids[:, 0] + 4)
+    assert np.all(ids[:, 0] < h) and np.all(ids[:, 1] == ids[:, 0] + h)
     assert np.allclose(w, 0.5, atol=1e-7)
