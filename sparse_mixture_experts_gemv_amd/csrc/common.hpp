@@ -11,6 +11,7 @@ namespace smoe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
@@ -29,6 +30,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // 4 * (l / 16) + {0, 1, 2, 3}.
 __device__ __forceinline__ f32x4 mfma_16x16x32(const uint4 &a, const uint4 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, each as 8
+// consecutive K values starting at K = 8 * (l / 32). D: lane l holds column
+// (l % 32), value v at row 8 (v / 4) + 4 (l / 32) + v % 4.
+__device__ __forceinline__ f32x16 mfma_32x32x16(const uint4 &a, const uint4 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
 }
 

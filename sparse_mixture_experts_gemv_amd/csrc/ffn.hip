@@ -152,7 +152,7 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
     pl.n_mtiles_up = tiles_upper_bound(N, E, pl.bm_up);
     pl.n_mtiles_down = tiles_upper_bound(N, E, pl.bm_down);
     pl.bn_up = (pl.kind_up == kKindPP) ? 128 : 128;
-    pl.bn_down = (pl.kind_down == kKindPP) ? 256 : 128;
+    pl.bn_down = (pl.kind_down == kKindReg) ? 128 : 256;
     pl.n_ntiles_up = (int)((F + pl.bn_up - 1) / pl.bn_up);
     pl.n_ntiles_down = (int)((D + pl.bn_down - 1) / pl.bn_down);
     size_t off = 0;
@@ -228,7 +228,7 @@ static void launch_gemm(int kind, int bm, const GemmParams &p, hipStream_t strea
             else launch_pp<128, 128, MODE, 32, 5>(p, stream);
         } else {
             if (bm == 256) launch_pp_streamk<256, 256, 32, 5>(p, stream);
-            else launch_pp<128, 256, MODE, 64, 3>(p, stream);
+            else launch_pp_streamk<128, 256, 64, 3>(p, stream);
         }
     } else {
         switch (bm) {

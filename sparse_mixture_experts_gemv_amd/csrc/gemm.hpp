@@ -39,7 +39,7 @@ struct GemmParams {
     const int32_t *slot_src;  // [S*k] slot -> flat route index
     const float *gate;        // [S*k] router weights (kDown)
     const int4 *tiles;        // [n_mtiles] (expert, row_begin, row_end, -) ; expert < 0 = empty
-    const uint32_t *order;    // [n_mtiles * n_ntiles] logical block -> mt | nt << 16 (nullptr: grouped order)
+    const uint32_t *order;    // [n_mtiles * n_ntiles] logical block -> mt | nt << kOrderMtBits (nullptr: grouped)
     const int *valid_mtiles;  // device count of non-empty M tiles (stream-K kernels)
     void *C;                  // h bf16 [S*k, N] / acc fp32 [S, N] / logits fp32 [S, N]
     int M;                    // rows (kLogits: S); A has M rows unless gathered
