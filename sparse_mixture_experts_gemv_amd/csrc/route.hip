@@ -6,11 +6,12 @@
 // the maximum subtracted:
 //
 //  * E <= 16 (route_small_kernel): the router GEMM is tiny (2 S D E FLOP)
-//    and the pass is bound by reading x once. Each wave scores R tokens:
-//    lane l owns columns d = 8 l + 512 j of D, keeps that slice of W_gate in
-//    registers while it walks the R token rows, then a wave reduction gives
-//    every lane all E logits and the top-k/softmax runs in registers. No
-//    logits buffer.
+//    and the pass is bound by reading x once. A workgroup scores 64 / E
+//    tokens: its 256 lanes split D into 8-column chunks, each lane holds the
+//    W_gate rows of its chunk in registers and accumulates all the
+//    workgroup's (token, expert) partial sums; a reduce-scatter over the wave
+//    and a fixed-order sum of the four waves in LDS give the logits, and one
+//    thread per token runs top-k and softmax. No logits buffer.
 //  * larger E: logits = x W_gate on bf16 MFMA with the ping-pong LDS-DMA GEMM
 //    (plain-rows mode), split over K so that a few thousand tokens still
 //    fill the GPU; every split writes its partial logits to the workspace and
@@ -27,7 +28,6 @@ namespace smoe {
 
 constexpr int kRouteMaxE = 256;
 constexpr int kRouteMaxK = 16;
-constexpr int kSmallR = 4;  // tokens per wave in the small-E path
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
@@ -37,92 +37,99 @@ __global__ __launch_bounds__(256) void route_small_kernel(const uint16_t *__rest
                                                           const uint16_t *__restrict__ wg, int S, int D, int k,
                                                           int32_t *__restrict__ ids, float *__restrict__ weights) {
     static_assert(E % 8 == 0 && E <= 16, "small-E path");
-    constexpr int R = kSmallR;
-    constexpr int EC = E / 8;  // 16-byte chunks per W_gate row
+    constexpr int TB = 64 / E;   // tokens per workgroup
+    constexpr int V = TB * E;    // partial sums per lane: V = 64, value t E + e
+    constexpr int EC = E / 8;    // 16-byte chunks per W_gate row
+    __shared__ float s_part[4][V];
+    __shared__ float s_logit[V];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = (blockIdx.x * 4 + wave) * R;
-    if (t0 >= S) return;
-    float acc[R][E];
+    const int t0 = blockIdx.x * TB;
+    float acc[V];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[r][e] = 0.f;
-    for (int d0 = lane * 8; d0 < D; d0 += 512) {
+    for (int v = 0; v < V; ++v) acc[v] = 0.f;
+    // chunk c covers columns 8 c .. 8 c + 7 of D; the 256 lanes of the
+    // workgroup take consecutive chunks, so every token row is read once,
+    // 1 KB contiguous per wave and load
+    for (int c = wave * 64 + lane; c < D / 8; c += 256) {
+        const int d0 = c * 8;
         uint4 w[8][EC];
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr)
 #pragma unroll
-            for (int c = 0; c < EC; ++c)
-                w[rr][c] = *reinterpret_cast<const uint4 *>(wg + (size_t)(d0 + rr) * E + c * 8);
+            for (int q = 0; q < EC; ++q)
+                w[rr][q] = *reinterpret_cast<const uint4 *>(wg + (size_t)(d0 + rr) * E + q * 8);
+        uint4 xv[TB];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int t = min(t0 + r, S - 1);  // rows past S repeat a valid row, never written
-            const uint4 xv = *reinterpret_cast<const uint4 *>(x + (size_t)t * D + d0);
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        for (int t = 0; t < TB; ++t) {
+            const int tt = min(t0 + t, S - 1);  // rows past S repeat a valid row, never written
+            xv[t] = *reinterpret_cast<const uint4 *>(x + (size_t)tt * D + d0);
+        }
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
 #pragma unroll
             for (int rr = 0; rr < 8; ++rr) {
                 const float xf = (rr & 1) ? bf16_hi(xw[rr >> 1]) : bf16_lo(xw[rr >> 1]);
 #pragma unroll
-                for (int c = 0; c < EC; ++c) {
-                    const uint32_t ww[4] = {w[rr][c].x, w[rr][c].y, w[rr][c].z, w[rr][c].w};
+                for (int q = 0; q < EC; ++q) {
+                    const uint32_t ww[4] = {w[rr][q].x, w[rr][q].y, w[rr][q].z, w[rr][q].w};
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const float wf = (q & 1) ? bf16_hi(ww[q >> 1]) : bf16_lo(ww[q >> 1]);
-                        acc[r][c * 8 + q] = fmaf(xf, wf, acc[r][c * 8 + q]);
+                    for (int e = 0; e < 8; ++e) {
+                        const float wf = (e & 1) ? bf16_hi(ww[e >> 1]) : bf16_lo(ww[e >> 1]);
+                        acc[t * E + q * 8 + e] = fmaf(xf, wf, acc[t * E + q * 8 + e]);
                     }
                 }
             }
         }
     }
+    // Reduce-scatter over the 64 lanes: at distance d the lane with bit d set
+    // keeps the upper half of its values and sends the lower half, so after
+    // six steps lane l holds the complete wave sum of value l.
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int d = 32, n = V; d >= 1; d >>= 1, n >>= 1) {
+        const bool upper = (lane & d) != 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            float v = acc[r][e];
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-            acc[r][e] = v;
+        for (int i = 0; i < n / 2; ++i) {
+            const float lo = acc[i], hi = acc[i + n / 2];
+            const float recv = __shfl_xor(upper ? lo : hi, d);
+            acc[i] = (upper ? hi : lo) + recv;
         }
-    // every lane now holds all logits; top-k + softmax (lane j writes rank j)
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int t = t0 + r;
-        if (t >= S) break;
+    }
+    static_assert(V == 64, "one value per lane after the reduce-scatter");
+    s_part[wave][lane] = acc[0];
+    __syncthreads();
+    if (threadIdx.x < V) {
+        const int v = threadIdx.x;
+        s_logit[v] = ((s_part[0][v] + s_part[1][v]) + s_part[2][v]) + s_part[3][v];
+    }
+    __syncthreads();
+    // top-k + softmax, one thread per token
+    if (threadIdx.x < TB && t0 + (int)threadIdx.x < S) {
+        const int t = t0 + threadIdx.x;
+        const float *lg = s_logit + threadIdx.x * E;
         unsigned taken = 0;
         float top[kRouteMaxK];
         int topi[kRouteMaxK];
+        for (int j = 0; j < k; ++j) {
+            float bv = -INFINITY;
+            int bi = -1;
 #pragma unroll
-        for (int j = 0; j < kRouteMaxK; ++j) {
-            top[j] = -INFINITY;
-            topi[j] = 0;
-            if (j < k) {
-                float bv = -INFINITY;
-                int bi = 0;
-                bool found = false;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    if (!((taken >> e) & 1u) && (!found || acc[r][e] > bv)) {
-                        bv = acc[r][e];
-                        bi = e;
-                        found = true;
-                    }
+            for (int e = 0; e < E; ++e) {
+                if (!((taken >> e) & 1u) && (bi < 0 || lg[e] > bv)) {
+                    bv = lg[e];
+                    bi = e;
                 }
-                taken |= 1u << bi;
-                top[j] = bv;
-                topi[j] = bi;
             }
+            taken |= 1u << bi;
+            top[j] = bv;
+            topi[j] = bi;
         }
         const float m = top[0];
         float z = 0.f;
-#pragma unroll
-        for (int j = 0; j < kRouteMaxK; ++j)
-            if (j < k) z += expf(top[j] - m);
-#pragma unroll
-        for (int j = 0; j < kRouteMaxK; ++j) {
-            if (j < k && lane == j) {
-                ids[(size_t)t * k + j] = topi[j];
-                weights[(size_t)t * k + j] = expf(top[j] - m) / z;
-            }
+        for (int j = 0; j < k; ++j) z += expf(top[j] - m);
+        for (int j = 0; j < k; ++j) {
+            ids[(size_t)t * k + j] = topi[j];
+            weights[(size_t)t * k + j] = expf(top[j] - m) / z;
         }
     }
 }
@@ -134,20 +141,32 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
     const int lane = threadIdx.x & 63;
     const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (s >= S) return;
-    float v[kRouteMaxE / 64];
+    constexpr int NV = kRouteMaxE / 64;
+    float v[NV];
     unsigned taken = 0;
 #pragma unroll
-    for (int i = 0; i < kRouteMaxE / 64; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E) {
-            float sum = 0.f;
-            for (int q = 0; q < nsplit; ++q) sum += partial[((size_t)q * S + s) * E + e];
-            v[i] = sum;
-        } else {
-            v[i] = -INFINITY;
-            taken |= 1u << i;
-        }
+    for (int i = 0; i < NV; ++i) {
+        v[i] = 0.f;
+        if (lane + 64 * i >= E) taken |= 1u << i;
     }
+    // splits are added in order; four splits of loads are in flight at a time
+    for (int q0 = 0; q0 < nsplit; q0 += 4) {
+        float t[4][NV];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = lane + 64 * i;
+                t[u][i] = (q0 + u < nsplit && e < E) ? partial[((size_t)(q0 + u) * S + s) * E + e] : 0.f;
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < NV; ++i) v[i] += t[u][i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        if ((taken >> i) & 1u) v[i] = -INFINITY;
     float top[kRouteMaxK];
     int topi[kRouteMaxK];
 #pragma unroll
@@ -237,7 +256,7 @@ size_t route_ws_bytes(int64_t S, int64_t E) {
 hipError_t launch_route(const uint16_t *x, const uint16_t *w_gate, int S, int D, int E, int k, int32_t *topk_ids,
                         float *topk_weights, void *workspace, hipStream_t stream) {
     if (E <= 16) {
-        const int blocks = (S + 4 * kSmallR - 1) / (4 * kSmallR);
+        const int blocks = (S + 64 / E - 1) / (64 / E);
         prof_begin(stream, kKRouteLogits);
         if (E == 8) route_small_kernel<8><<<blocks, 256, 0, stream>>>(x, w_gate, S, D, k, topk_ids, topk_weights);
         else route_small_kernel<16><<<blocks, 256, 0, stream>>>(x, w_gate, S, D, k, topk_ids, topk_weights);
