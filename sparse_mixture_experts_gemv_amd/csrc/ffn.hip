@@ -127,13 +127,13 @@ __global__ __launch_bounds__(256) void acc_finalize_kernel(const float4 *__restr
 // Kernel choice per GEMM from the mean rows per expert (known on the host
 // without reading the device-side counts):
 //   >= 192 rows: ping-pong LDS-DMA kernel, 256-row tiles
-//   >=  96 rows: ping-pong LDS-DMA kernel, 128-row tiles
+//   >=  96 rows: ping-pong LDS-DMA kernel, 192-row tiles
 //   fewer:       register-staged kernel with 64 / 32 / 16-row tiles
 enum GemmKind { kKindReg = 0, kKindPP = 1 };
 
 static void pick_gemm(int64_t avg, int &kind, int &bm) {
     if (avg >= 192) { kind = kKindPP; bm = 256; }
-    else if (avg >= 96) { kind = kKindPP; bm = 128; }
+    else if (avg >= 96) { kind = kKindPP; bm = 192; }
     else if (avg >= 48) { kind = kKindReg; bm = 64; }
     else if (avg >= 24) { kind = kKindReg; bm = 32; }
     else { kind = kKindReg; bm = 16; }
@@ -151,7 +151,7 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
     pick_gemm(avg, pl.kind_down, pl.bm_down);
     pl.n_mtiles_up = tiles_upper_bound(N, E, pl.bm_up);
     pl.n_mtiles_down = tiles_upper_bound(N, E, pl.bm_down);
-    pl.bn_up = (pl.kind_up == kKindPP) ? 128 : 128;
+    pl.bn_up = 128;
     pl.bn_down = (pl.kind_down == kKindReg) ? 128 : 256;
     pl.n_ntiles_up = (int)((F + pl.bn_up - 1) / pl.bn_up);
     pl.n_ntiles_down = (int)((D + pl.bn_down - 1) / pl.bn_down);
@@ -225,10 +225,10 @@ static void launch_gemm(int kind, int bm, const GemmParams &p, hipStream_t strea
     if (kind == kKindPP) {
         if constexpr (MODE == kGateUp) {
             if (bm == 256) launch_pp<256, 128, MODE, 64, 2>(p, stream);
-            else launch_pp<128, 128, MODE, 32, 5>(p, stream);
+            else launch_pp<192, 128, MODE, 32, 5>(p, stream);
         } else {
             if (bm == 256) launch_pp_streamk<256, 256, 32, 5>(p, stream);
-            else launch_pp_streamk<128, 256, 64, 3>(p, stream);
+            else launch_pp_streamk<192, 256, 32, 5>(p, stream);
         }
     } else {
         switch (bm) {
