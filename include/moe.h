@@ -122,12 +122,20 @@ int moe_sparse_map(const int32_t *topk_ids, int32_t S, int32_t k, int32_t E, int
                    size_t workspace_bytes, void *stream);
 
 /*
- * Workspace bytes moe_scatter_ffn_fwd needs: the intermediate h [S*k, F]
- * bf16 in slot order, the fp32 combine accumulator [S, D] and a tile table.
- * No term is proportional to S*k*D: token rows are never replicated.
- * Pure host function.
+ * Workspace bytes for the default combine of moe_scatter_ffn_fwd: the
+ * intermediate h [S*k, F] bf16 in slot order, the router-weighted down
+ * projection of every route y [S*k, D] fp32 and a tile table. The input
+ * token rows are never replicated (x is read in place by index). Pure host
+ * function.
  */
 size_t moe_scatter_ffn_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k);
+
+/*
+ * Smaller workspace that selects the atomic scatter-add combine: h, an fp32
+ * token accumulator [S, D] and a tile table. No term is proportional to
+ * S*k*D. Pure host function.
+ */
+size_t moe_scatter_ffn_workspace_bytes_atomic(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k);
 
 /*
  * Scattered SwiGLU experts with weighted scatter-add combine (ScatterMoE
@@ -138,13 +146,21 @@ size_t moe_scatter_ffn_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t 
  * For every slot r of expert e (offsets[e] <= r < offsets[e+1]), with
  * f = slot_src[r] and token t = f / k:
  *   h[r, :]  = bf16( SiLU(x[t, :] W1[e]) * (x[t, :] W3[e]) )   (fp32 sums)
- *   acc[t,:] += topk_weights[f] * (h[r, :] W2[e])               (fp32)
- *   out[t,:]  = bf16(acc[t, :])     (round to nearest even, once)
+ *   y_f      = topk_weights[f] * (h[r, :] W2[e])                 (fp32)
+ *   out[t,:] = bf16( sum over the k routes f of token t of y_f )  (rounded once)
+ * The combine runs one of two ways, chosen by workspace_bytes:
+ *  - workspace_bytes >= moe_scatter_ffn_workspace_bytes(): the down
+ *    projection stores y_f to row f of an fp32 [S*k, D] buffer and a combine
+ *    pass adds the k rows of each token in the order j = 0 .. k-1. The
+ *    output is bitwise reproducible from run to run.
+ *  - else, workspace_bytes >= moe_scatter_ffn_workspace_bytes_atomic(): the
+ *    down projection adds y_f into an fp32 [S, D] token accumulator with
+ *    atomics (the in-place scatter-add of the ScatterMoE kernel); the order
+ *    of the k additions is not fixed, so the last fp32 bit may vary.
  * x [S, D] bf16; w1, w3 [E, D, F] bf16; w2 [E, F, D] bf16 (each expert's
  * matrix is [D_in, D_out] with D_out contiguous); topk_weights [S, k] fp32;
  * expert_offsets [E+1] and slot_src [S*k] from moe_sparse_map on the same
- * ids; out [S, D] bf16 (fully written; tokens with no route get zeros).
- * workspace >= moe_scatter_ffn_workspace_bytes(S, D, F, E, k).
+ * ids; out [S, D] bf16 (fully written).
  * Limits: D % 64 == 0, F % 64 == 0, E <= 1024, S*D < 2^30, D*F < 2^30
  * (32-bit buffer offsets), D <= 2^19, F <= 2^19 and fewer than 2^20 - 1 row
  * tiles (always true for S*k < 2^26): else UNSUPPORTED.

@@ -3,7 +3,8 @@ kernels behind a C ABI (include/moe.h), called through a thin ctypes binding.
 
     moe_route_topk       router top-k + softmax
     moe_sparse_map       per-expert histogram, exclusive scan, stable route -> slot map
-    moe_scatter_ffn_fwd  gathered SwiGLU experts + router-weighted scatter-add combine
+    moe_scatter_ffn_fwd  gathered SwiGLU experts + router-weighted combine (ordered per-route
+                         rows by default, fp32 atomic scatter-add with atomic=True)
 """
 from ._lib import (MoEError, MoELayer, layer_fwd, load, profile_start, profile_stop, moe_route_topk, moe_scatter_ffn_fwd, moe_sparse_map,
                    route_workspace_bytes, scatter_ffn_workspace_bytes, sparse_map_workspace_bytes, status_str)

@@ -28,6 +28,7 @@ SIGNATURES = {
     "moe_sparse_map_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "moe_sparse_map": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_scatter_ffn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "moe_scatter_ffn_workspace_bytes_atomic": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_scatter_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ,
                                            _P]),
     "moe_profile_start": (ctypes.c_int, [ctypes.c_int]),
@@ -106,8 +107,12 @@ def sparse_map_workspace_bytes(S: int, k: int, E: int) -> int:
     return int(load().moe_sparse_map_workspace_bytes(S, k, E))
 
 
-def scatter_ffn_workspace_bytes(S: int, D: int, F: int, E: int, k: int) -> int:
-    return int(load().moe_scatter_ffn_workspace_bytes(S, D, F, E, k))
+def scatter_ffn_workspace_bytes(S: int, D: int, F: int, E: int, k: int, atomic: bool = False) -> int:
+    """Workspace for moe_scatter_ffn_fwd: per-route fp32 rows + ordered combine (default) or,
+    with atomic=True, the smaller fp32 token accumulator of the atomic scatter-add."""
+    lib = load()
+    fn = lib.moe_scatter_ffn_workspace_bytes_atomic if atomic else lib.moe_scatter_ffn_workspace_bytes
+    return int(fn(S, D, F, E, k))
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
@@ -163,8 +168,11 @@ def moe_sparse_map(topk_ids: torch.Tensor, E: int, out: Optional[Tuple[torch.Ten
 def moe_scatter_ffn_fwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
                         topk_weights: torch.Tensor, expert_offsets: torch.Tensor, slot_src: torch.Tensor,
                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                        stream=None) -> torch.Tensor:
-    """SwiGLU experts on gathered rows + weighted scatter-add combine -> out bf16 [S, D]."""
+                        stream=None, atomic: bool = False) -> torch.Tensor:
+    """SwiGLU experts on gathered rows + router-weighted combine -> out bf16 [S, D].
+
+    atomic=False: per-route rows and an ordered combine (bitwise reproducible);
+    atomic=True: fp32 atomic scatter-add into a token accumulator (smaller workspace)."""
     S, D = x.shape
     E, D2, F = w1.shape
     k = topk_weights.shape[1]
@@ -178,10 +186,12 @@ def moe_scatter_ffn_fwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2:
     if out is None:
         out = torch.empty((S, D), dtype=torch.bfloat16, device=x.device)
     _dev(out, torch.bfloat16, "out", (S, D))
-    ws = _workspace(scatter_ffn_workspace_bytes(S, D, F, E, k), x.device, workspace)
+    need = scatter_ffn_workspace_bytes(S, D, F, E, k, atomic)
+    ws = _workspace(need, x.device, workspace)
+    # the library picks the combine from the byte count it is given
     _check(load().moe_scatter_ffn_fwd(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(topk_weights),
                                       _ptr(expert_offsets), _ptr(slot_src), S, D, F, E, k, _ptr(out), _ptr(ws),
-                                      ws.numel() * ws.element_size(), _stream(stream)), "moe_scatter_ffn_fwd")
+                                      need, _stream(stream)), "moe_scatter_ffn_fwd")
     return out
 
 
@@ -192,8 +202,9 @@ class MoELayer:
     route -> sparse map -> scattered FFN. Nothing is allocated per call.
     """
 
-    def __init__(self, w_gate, w1, w3, w2, k: int, S: int):
+    def __init__(self, w_gate, w1, w3, w2, k: int, S: int, atomic: bool = False):
         self.w_gate, self.w1, self.w3, self.w2, self.k, self.S = w_gate, w1, w3, w2, k, S
+        self.atomic = atomic
         E, D, F = w1.shape
         self.E, self.D, self.F = E, D, F
         dev = w1.device
@@ -203,7 +214,7 @@ class MoELayer:
                     torch.empty(S * k, dtype=torch.int32, device=dev), torch.empty(S * k, dtype=torch.int32, device=dev))
         self.out = torch.empty((S, D), dtype=torch.bfloat16, device=dev)
         nbytes = max(route_workspace_bytes(S, E), sparse_map_workspace_bytes(S, k, E),
-                     scatter_ffn_workspace_bytes(S, D, F, E, k))
+                     scatter_ffn_workspace_bytes(S, D, F, E, k, atomic))
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
     def forward(self, x: torch.Tensor, topk: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, stream=None):
@@ -214,7 +225,7 @@ class MoELayer:
             ids, weights = topk
         moe_sparse_map(ids, self.E, self.map, self.ws, stream)
         moe_scatter_ffn_fwd(x, self.w1, self.w3, self.w2, weights, self.map[1], self.map[3], self.out, self.ws,
-                            stream)
+                            stream, self.atomic)
         return self.out
 
 

@@ -73,7 +73,12 @@ int moe_sparse_map(const int32_t *topk_ids, int32_t S, int32_t k, int32_t E, int
 
 size_t moe_scatter_ffn_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k) {
     if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1) return 0;
-    return smoe::ffn_plan(S, D, F, E, k).ws_bytes;
+    return smoe::ffn_plan(S, D, F, E, k, false).ws_bytes;
+}
+
+size_t moe_scatter_ffn_workspace_bytes_atomic(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k) {
+    if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1) return 0;
+    return smoe::ffn_plan(S, D, F, E, k, true).ws_bytes;
 }
 
 int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
@@ -92,11 +97,17 @@ int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
     // 32-bit buffer offsets: x, each expert matrix and each tile's rows of h stay below 2 GiB
     if (N >= ((int64_t)1 << 31) || (int64_t)S * D >= ((int64_t)1 << 30) || (int64_t)D * F >= ((int64_t)1 << 30))
         return MOE_ERR_UNSUPPORTED;
-    const smoe::FfnPlan plan = smoe::ffn_plan(S, D, F, E, k);
-    if (!smoe::ffn_plan_fits(plan)) return MOE_ERR_UNSUPPORTED;
-    if (workspace_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    // the per-route-rows path when the workspace holds its fp32 [S*k, D]
+    // rows, else the atomic scatter-add path
+    const smoe::FfnPlan rows = smoe::ffn_plan(S, D, F, E, k, false);
+    const smoe::FfnPlan atomic = smoe::ffn_plan(S, D, F, E, k, true);
+    if (!smoe::ffn_plan_fits(rows)) return MOE_ERR_UNSUPPORTED;
+    bool use_atomic;
+    if (workspace_bytes >= rows.ws_bytes) use_atomic = false;
+    else if (workspace_bytes >= atomic.ws_bytes) use_atomic = true;
+    else return MOE_ERR_WORKSPACE_TOO_SMALL;
     return finish(smoe::launch_scatter_ffn(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, S, D, F, E, k, out,
-                                           workspace, reinterpret_cast<hipStream_t>(stream)));
+                                           workspace, use_atomic, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

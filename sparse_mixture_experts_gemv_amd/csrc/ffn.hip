@@ -124,6 +124,30 @@ __global__ __launch_bounds__(256) void acc_finalize_kernel(const float4 *__restr
     }
 }
 
+// out[t, :] = bf16(sum_j y[t k + j, :]) for the per-route rows y (route f =
+// t k + j keeps the k rows of a token adjacent); the k terms are added in
+// the order j = 0 .. k-1, so the result does not depend on scheduling.
+__global__ __launch_bounds__(256) void combine_rows_kernel(const float4 *__restrict__ y, uint2 *__restrict__ out,
+                                                           int S, int D4, int k) {
+    const size_t n4 = (size_t)S * D4;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const size_t t = i / D4, c = i - t * D4;
+        const float4 *src = y + t * k * D4 + c;
+        float4 v = src[0];
+        for (int j = 1; j < k; ++j) {
+            const float4 u = src[(size_t)j * D4];
+            v.x += u.x;
+            v.y += u.y;
+            v.z += u.z;
+            v.w += u.w;
+        }
+        const uint32_t lo = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
+        out[i] = make_uint2(lo, hi);
+    }
+}
+
 // Kernel choice per GEMM from the mean rows per expert (known on the host
 // without reading the device-side counts):
 //   >= 192 rows: ping-pong LDS-DMA kernel, 256-row tiles
@@ -143,8 +167,9 @@ static int tiles_upper_bound(int64_t N, int64_t E, int bm) {
     return (int)((N + std::min(E, N) * (bm - 1)) / bm);
 }
 
-FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
+FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k, bool atomic) {
     FfnPlan pl;
+    pl.atomic = atomic;
     const int64_t N = S * k;
     const int64_t avg = N / std::max<int64_t>(E, 1);
     pick_gemm(avg, pl.kind_up, pl.bm_up);
@@ -169,7 +194,7 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
     pl.h_off = off;
     off += align_up((size_t)N * (size_t)F * 2);
     pl.acc_off = off;
-    off += align_up((size_t)S * (size_t)D * 4);
+    off += align_up((size_t)(atomic ? S : S * k) * (size_t)D * 4);
     pl.ws_bytes = off;
     return pl;
 }
@@ -209,6 +234,16 @@ static int device_cus() {
     return cached[dev];
 }
 
+// Per-route-rows down GEMM: one persistent workgroup per CU walking whole
+// tiles (the epilogue is a plain store, so tiles are never split).
+template <int BM, int BN, int BK, int STAGES>
+static void launch_pp_persistent_rows(const GemmParams &p0, hipStream_t stream) {
+    GemmParams p = p0;
+    p.n_ntiles = (p.N + BN - 1) / BN;
+    if (p.n_mtiles * p.n_ntiles == 0) return;
+    grouped_gemm_pp_persistent_kernel<BM, BN, kDownRows, BK, STAGES><<<device_cus(), 512, 0, stream>>>(p);
+}
+
 // Stream-K down GEMM: one persistent workgroup per CU (160 KB of LDS each).
 template <int BM, int BN, int BK, int STAGES>
 static void launch_pp_streamk(const GemmParams &p0, hipStream_t stream) {
@@ -226,9 +261,12 @@ static void launch_gemm(int kind, int bm, const GemmParams &p, hipStream_t strea
         if constexpr (MODE == kGateUp) {
             if (bm == 256) launch_pp<256, 128, MODE, 64, 2>(p, stream);
             else launch_pp<192, 128, MODE, 32, 5>(p, stream);
-        } else {
+        } else if constexpr (MODE == kDown) {
             if (bm == 256) launch_pp_streamk<256, 256, 32, 5>(p, stream);
             else launch_pp_streamk<192, 256, 32, 5>(p, stream);
+        } else {
+            if (bm == 256) launch_pp_persistent_rows<256, 256, 32, 5>(p, stream);
+            else launch_pp_persistent_rows<192, 256, 32, 5>(p, stream);
         }
     } else {
         switch (bm) {
@@ -242,9 +280,9 @@ static void launch_gemm(int kind, int bm, const GemmParams &p, hipStream_t strea
 
 hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                               const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
-                              int S, int D, int F, int E, int k, uint16_t *out, void *workspace,
+                              int S, int D, int F, int E, int k, uint16_t *out, void *workspace, bool atomic,
                               hipStream_t stream) {
-    const FfnPlan pl = ffn_plan(S, D, F, E, k);
+    const FfnPlan pl = ffn_plan(S, D, F, E, k, atomic);
     char *ws = reinterpret_cast<char *>(workspace);
     int4 *tiles_up = reinterpret_cast<int4 *>(ws + pl.tiles_up_off);
     int4 *tiles_down = reinterpret_cast<int4 *>(ws + pl.tiles_down_off);
@@ -272,9 +310,11 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     prof_begin(stream, kKTileTable);
     tile_table_kernel<<<1, 1024, 0, stream>>>(expert_offsets, E, N, ta);
     prof_end(stream, kKTileTable);
-    prof_begin(stream, kKAccZero);
-    acc_zero_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<float4 *>(acc), n4);
-    prof_end(stream, kKAccZero);
+    if (atomic) {
+        prof_begin(stream, kKAccZero);
+        acc_zero_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<float4 *>(acc), n4);
+        prof_end(stream, kKAccZero);
+    }
 
     GemmParams p{};
     p.slot_src = slot_src;
@@ -296,7 +336,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.K = D;
     launch_gemm<kGateUp>(pl.kind_up, pl.bm_up, p, stream);
 
-    // down + scatter-add: A = h (slot order), K = F, N = D
+    // down + scatter-add (atomic) or per-route rows: A = h (slot order), K = F, N = D
     p.tiles = tiles_down;
     p.order = order_down;
     p.valid_mtiles = valid_counts + 1;
@@ -307,12 +347,19 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.C = acc;
     p.N = D;
     p.K = F;
-    launch_gemm<kDown>(pl.kind_down, pl.bm_down, p, stream);
-
-    prof_begin(stream, kKFinalize);
-    acc_finalize_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
-                                                                    reinterpret_cast<uint2 *>(out), n4);
-    prof_end(stream, kKFinalize);
+    if (atomic) {
+        launch_gemm<kDown>(pl.kind_down, pl.bm_down, p, stream);
+        prof_begin(stream, kKFinalize);
+        acc_finalize_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
+                                                                        reinterpret_cast<uint2 *>(out), n4);
+        prof_end(stream, kKFinalize);
+    } else {
+        launch_gemm<kDownRows>(pl.kind_down, pl.bm_down, p, stream);
+        prof_begin(stream, kKCombine);
+        combine_rows_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
+                                                                        reinterpret_cast<uint2 *>(out), S, D / 4, k);
+        prof_end(stream, kKCombine);
+    }
     return hipGetLastError();
 }
 

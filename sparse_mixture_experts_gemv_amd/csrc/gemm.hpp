@@ -7,12 +7,16 @@
 // itself (contiguous A) or the token of the slot (gathered A: token rows of
 // X read in place, never copied).
 //
-// Three epilogues:
+// Four epilogues:
 //   kGateUp   two B matrices (W1, W3) share every A tile; the tile writes
 //             h = bf16(SiLU(A W1) * (A W3)) in slot order (fused gate+up).
 //   kDown     one B matrix (W2); the tile scales each row by its route's
 //             router weight and atomically adds into the fp32 token
 //             accumulator (scatter-add combine).
+//   kDownRows one B matrix (W2); the tile scales each row by its route's
+//             router weight and stores it, fp32, to row f of a per-route
+//             buffer (f = the slot's flat route index, so the k rows of a
+//             token are adjacent); a combine pass sums them per token.
 //   kLogits   one B matrix (W_gate), no experts; fp32 store (router logits).
 //
 // Weights are [E, K, N] with N contiguous. MFMA wants K-contiguous operands,
@@ -30,18 +34,18 @@
 
 namespace smoe {
 
-enum GemmMode { kGateUp = 0, kDown = 1, kLogits = 2 };
+enum GemmMode { kGateUp = 0, kDown = 1, kLogits = 2, kDownRows = 3 };
 
 struct GemmParams {
-    const uint16_t *A;        // X [S, K] (kGateUp, kLogits) or h [S*k, K] (kDown)
+    const uint16_t *A;        // X [S, K] (kGateUp, kLogits) or h [S*k, K] (kDown, kDownRows)
     const uint16_t *B0;       // W1 / W2 / W_gate: [E, K, N]
     const uint16_t *B1;       // W3 (kGateUp only)
     const int32_t *slot_src;  // [S*k] slot -> flat route index
-    const float *gate;        // [S*k] router weights (kDown)
+    const float *gate;        // [S*k] router weights (kDown, kDownRows)
     const int4 *tiles;        // [n_mtiles] (expert, row_begin, row_end, -) ; expert < 0 = empty
     const uint32_t *order;    // [n_mtiles * n_ntiles] logical block -> mt | nt << kOrderMtBits (nullptr: grouped)
     const int *valid_mtiles;  // device count of non-empty M tiles (stream-K kernels)
-    void *C;                  // h bf16 [S*k, N] / acc fp32 [S, N] / logits fp32 [S, N]
+    void *C;                  // h bf16 [S*k, N] / acc fp32 [S, N] / y fp32 [S*k, N] / logits fp32 [S, N]
     int M;                    // rows (kLogits: S); A has M rows unless gathered
     int A_rows;               // rows of A (gathered: S)
     int N;                    // output columns
@@ -266,6 +270,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams p) {
                 for (int j = 0; j < NT; ++j) {
                     const int col = wn * WTN + j * 16 + col_in_tile;
                     if (n0 + col < N) atomicAdd(accp + col, w * acc[0][i][j][r]);
+                }
+            } else if (MODE == kDownRows) {
+                const int f = p.slot_src[slot];
+                const float w = p.gate[f];
+                float *yp = reinterpret_cast<float *>(p.C) + (size_t)f * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) yp[col] = w * acc[0][i][j][r];
                 }
             } else {
                 float *out = reinterpret_cast<float *>(p.C) + (size_t)slot * N + n0;

@@ -323,6 +323,15 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
                     const int col = wn * WTN + j * 16 + col_in_tile;
                     if (n0 + col < N) atomicAdd(accp + col, w * acc[0][i][j][r]);
                 }
+            } else if (MODE == kDownRows) {
+                const int f = p.slot_src[slot];
+                const float w = p.gate[f];
+                float *yp = reinterpret_cast<float *>(p.C) + (size_t)f * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) yp[col] = w * acc[0][i][j][r];
+                }
             } else {
                 float *out = reinterpret_cast<float *>(p.C) + (size_t)slot * N + n0;
 #pragma unroll
@@ -342,6 +351,22 @@ __global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p
     int mt, nt;
     if (!decode_tile(p, mt, nt)) return;
     pp_tile<BM, BN, MODE, BK, STAGES>(p, smem, mt, nt, 0, p.K / BK);
+}
+
+// Persistent tile-granular form: one workgroup per CU walks the valid
+// blocks of the order table with stride gridDim.x (each XCD takes one
+// contiguous run of the order per round), so a tile's epilogue stores drain
+// while the same workgroup already streams its next tile.
+template <int BM, int BN, int MODE, int BK, int STAGES>
+__global__ __launch_bounds__(512) void grouped_gemm_pp_persistent_kernel(const GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[PPGeom<BM, BN, MODE, BK, STAGES>::SMEM];
+    const int total = (*p.valid_mtiles) * p.n_ntiles;
+    const int G = gridDim.x;
+    for (int L = xcd_remap(blockIdx.x, G); L < total; L += G) {
+        const uint32_t v = p.order[L];
+        const int mt = (int)(v & kOrderMtMask), nt = (int)(v >> kOrderMtBits);
+        if (mt < p.n_mtiles) pp_tile<BM, BN, MODE, BK, STAGES>(p, smem, mt, nt, 0, p.K / BK);
+    }
 }
 
 // Persistent stream-K form for the down GEMM, whose epilogue is an atomic

@@ -30,14 +30,16 @@ constexpr uint32_t kOrderMtMask = (1u << kOrderMtBits) - 1u;
 constexpr int kOrderMaxNtiles = 1 << (32 - kOrderMtBits);
 
 struct FfnPlan {
+    bool atomic;               // down GEMM: fp32 atomic scatter-add (else per-route rows + combine)
     int kind_up, bm_up;        // gate+up GEMM: kernel kind and rows per M tile
     int kind_down, bm_down;    // down GEMM
     int bn_up, bn_down;        // columns per N tile
     int n_mtiles_up, n_mtiles_down;  // upper bounds on M tiles over all experts
     int n_ntiles_up, n_ntiles_down;
+    // acc_off: fp32 [S, D] token accumulator (atomic) or fp32 [S*k, D] per-route rows
     size_t tiles_up_off, tiles_down_off, order_up_off, order_down_off, counts_off, h_off, acc_off, ws_bytes;
 };
-FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k);
+FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k, bool atomic);
 // Whether the plan's tile counts fit the block-order entries.
 inline bool ffn_plan_fits(const FfnPlan &pl) {
     return pl.n_mtiles_up < (int)kOrderMtMask && pl.n_mtiles_down < (int)kOrderMtMask &&
@@ -45,7 +47,7 @@ inline bool ffn_plan_fits(const FfnPlan &pl) {
 }
 hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                               const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
-                              int S, int D, int F, int E, int k, uint16_t *out, void *workspace,
+                              int S, int D, int F, int E, int k, uint16_t *out, void *workspace, bool atomic,
                               hipStream_t stream);
 
 // ---- router ----

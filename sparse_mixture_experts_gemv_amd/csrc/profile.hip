@@ -36,7 +36,8 @@ Profiler &prof() {
 
 const char *kNames[kNumKernelIds] = {"route_logits_gemm", "route_topk_softmax", "smap_hist",  "smap_rowscan",
                                      "smap_assign",       "smap_empty",         "ffn_tile_table", "ffn_acc_zero",
-                                     "ffn_gate_up_gemm",  "ffn_down_scatter_gemm", "ffn_finalize"};
+                                     "ffn_gate_up_gemm",  "ffn_down_scatter_gemm", "ffn_finalize",
+                                     "ffn_combine"};
 
 }  // namespace
 

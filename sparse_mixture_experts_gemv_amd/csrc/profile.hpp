@@ -19,6 +19,7 @@ enum KernelId {
     kKGateUp,
     kKDown,
     kKFinalize,
+    kKCombine,
     kNumKernelIds
 };
 

@@ -28,7 +28,7 @@ def header_functions():
 def test_exports_every_declared_symbol(lib):
     import sparse_mixture_experts_gemv_amd._lib as b
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.SIGNATURES)
@@ -94,8 +94,10 @@ def test_ffn_validation(lib):
 def test_workspace_has_no_token_replication(lib):
     """Closed form on the ScatterMoE guide's pipeline figure: replicating the
     tokens costs S*k*D*2 bytes (67.1 MB at S=D=4096, k=2, fp16; 2.15 GB over
-    32 layers). The FFN workspace grows with D only through the fp32 [S, D]
-    accumulator, never through an [S*k, D] term."""
+    32 layers). The atomic-combine workspace grows with D only through the
+    fp32 [S, D] accumulator, never through an [S*k, D] term; the default
+    workspace adds exactly the fp32 per-route output rows [S*k, D] of the
+    ordered combine (outputs of the down projection, not copies of x)."""
     fig = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
     rep = fig["replication_bytes_per_layer"]
     nbytes = rep["S"] * rep["k"] * rep["D"] * rep["bytes_per_element"]
@@ -103,8 +105,11 @@ def test_workspace_has_no_token_replication(lib):
     assert round(32 * nbytes / 1e9, 2) == fig["replication_bytes_32_layers"]["value_GB"]
     oh = fig["one_hot_register_elements"]
     assert oh["block_size"] * oh["num_experts"] == oh["value"]
-    ws = lambda S, D, F, E, k: lib.moe_scatter_ffn_workspace_bytes(S, D, F, E, k)
+    ws = lambda S, D, F, E, k: lib.moe_scatter_ffn_workspace_bytes_atomic(S, D, F, E, k)
+    rows = lambda S, D, F, E, k: lib.moe_scatter_ffn_workspace_bytes(S, D, F, E, k)
     for (S, F, E, k) in [(4096, 14336, 8, 2), (4096, 2048, 256, 8), (8192, 2880, 128, 4)]:
+        for D in (4096, 8192):
+            assert rows(S, D, F, E, k) - ws(S, D, F, E, k) == (S * k - S) * D * 4
         d1, d2 = ws(S, 4096, F, E, k), ws(S, 8192, F, E, k)
         # growth with D: the fp32 accumulator plus a block-order table of a few KB,
         # nowhere near the S*k*D*2 bytes a token copy would add
