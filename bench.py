@@ -1,9 +1,9 @@
 """Benchmark of the dropless sparse-MoE forward on one MI355X.
 
 A step is one whole forward pass on resident inputs: router top-k + softmax,
-sparse map, gathered gate+up GEMM with SwiGLU, down GEMM with weighted
-scatter-add, and the bf16 finalize -- the three C-ABI calls back to back on
-one stream. The default workload is the Mixtral-8x7B-shaped layer
+sparse map, gathered gate+up GEMM with SwiGLU, down GEMM storing the
+router-weighted per-route rows, and the ordered combine into bf16 tokens --
+the three C-ABI calls back to back on one stream. The default workload is the Mixtral-8x7B-shaped layer
 (S=4096, D=4096, F=14336, E=8, k=2) with seeded synthetic inputs.
 
 Prints one JSON line with the whole-job throughput (tokens/s), the
