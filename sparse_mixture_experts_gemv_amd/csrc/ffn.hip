@@ -213,15 +213,6 @@ static void launch_reg(const GemmParams &p0, hipStream_t stream) {
     grouped_gemm_kernel<BM, BN, WM, WN, MODE><<<blocks, 256, 0, stream>>>(p);
 }
 
-template <int BM, int BN, int MODE, int BK, int STAGES>
-static void launch_pp(const GemmParams &p0, hipStream_t stream) {
-    GemmParams p = p0;
-    p.n_ntiles = (p.N + BN - 1) / BN;
-    const int blocks = p.n_mtiles * p.n_ntiles;
-    if (blocks == 0) return;
-    grouped_gemm_pp_kernel<BM, BN, MODE, BK, STAGES><<<blocks, 512, 0, stream>>>(p);
-}
-
 static int device_cus() {
     static int cached[64] = {0};
     int dev = 0;
@@ -234,14 +225,15 @@ static int device_cus() {
     return cached[dev];
 }
 
-// Per-route-rows down GEMM: one persistent workgroup per CU walking whole
-// tiles (the epilogue is a plain store, so tiles are never split).
-template <int BM, int BN, int BK, int STAGES>
-static void launch_pp_persistent_rows(const GemmParams &p0, hipStream_t stream) {
+// Gate+up and per-route-rows down GEMMs: one persistent workgroup per CU
+// walking whole tiles of the block order (plain-store epilogues, so tiles are
+// never split); a tile's epilogue overlaps the next tile's first loads.
+template <int BM, int BN, int MODE, int BK, int STAGES>
+static void launch_pp_persistent(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
     p.n_ntiles = (p.N + BN - 1) / BN;
     if (p.n_mtiles * p.n_ntiles == 0) return;
-    grouped_gemm_pp_persistent_kernel<BM, BN, kDownRows, BK, STAGES><<<device_cus(), 512, 0, stream>>>(p);
+    grouped_gemm_pp_persistent_kernel<BM, BN, MODE, BK, STAGES><<<device_cus(), 512, 0, stream>>>(p);
 }
 
 // Stream-K down GEMM: one persistent workgroup per CU (160 KB of LDS each).
@@ -259,14 +251,14 @@ static void launch_gemm(int kind, int bm, const GemmParams &p, hipStream_t strea
     prof_begin(stream, kid);
     if (kind == kKindPP) {
         if constexpr (MODE == kGateUp) {
-            if (bm == 256) launch_pp<256, 128, MODE, 64, 2>(p, stream);
-            else launch_pp<192, 128, MODE, 32, 5>(p, stream);
+            if (bm == 256) launch_pp_persistent<256, 128, MODE, 64, 2>(p, stream);
+            else launch_pp_persistent<192, 128, MODE, 32, 5>(p, stream);
         } else if constexpr (MODE == kDown) {
             if (bm == 256) launch_pp_streamk<256, 256, 32, 5>(p, stream);
             else launch_pp_streamk<192, 256, 32, 5>(p, stream);
         } else {
-            if (bm == 256) launch_pp_persistent_rows<256, 256, 32, 5>(p, stream);
-            else launch_pp_persistent_rows<192, 256, 32, 5>(p, stream);
+            if (bm == 256) launch_pp_persistent<256, 256, MODE, 32, 5>(p, stream);
+            else launch_pp_persistent<192, 256, MODE, 32, 5>(p, stream);
         }
     } else {
         switch (bm) {
@@ -334,6 +326,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.M = N;
     p.N = F;
     p.K = D;
+    p.valid_mtiles = valid_counts;
     launch_gemm<kGateUp>(pl.kind_up, pl.bm_up, p, stream);
 
     // down + scatter-add (atomic) or per-route rows: A = h (slot order), K = F, N = D
