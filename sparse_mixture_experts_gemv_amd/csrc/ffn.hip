@@ -148,19 +148,16 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float4 *__restr
     }
 }
 
-// Kernel choice per GEMM from the mean rows per expert (known on the host
-// without reading the device-side counts):
-//   >= 192 rows: ping-pong LDS-DMA kernel, 256-row tiles
-//   >=  96 rows: ping-pong LDS-DMA kernel, 192-row tiles
-//   fewer:       register-staged kernel with 64 / 32 / 16-row tiles
-enum GemmKind { kKindReg = 0, kKindPP = 1 };
-
-static void pick_gemm(int64_t avg, int &kind, int &bm) {
-    if (avg >= 192) { kind = kKindPP; bm = 256; }
-    else if (avg >= 96) { kind = kKindPP; bm = 192; }
-    else if (avg >= 48) { kind = kKindReg; bm = 64; }
-    else if (avg >= 24) { kind = kKindReg; bm = 32; }
-    else { kind = kKindReg; bm = 16; }
+// Tile height per GEMM from the mean rows per expert (known on the host
+// without reading the device-side counts): 256 rows from 192 up, 192 rows
+// from 96 (an expert of ~128 +- 3 sigma rows fits one tile, so its weights
+// stream once), 64 rows from 48, else 32 rows (decode-sized batches: the
+// weights dominate and a shallow tile keeps the MFMA work small).
+static int pick_bm(int64_t avg) {
+    if (avg >= 192) return 256;
+    if (avg >= 96) return 192;
+    if (avg >= 48) return 64;
+    return 32;
 }
 
 static int tiles_upper_bound(int64_t N, int64_t E, int bm) {
@@ -172,12 +169,11 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k, bool ato
     pl.atomic = atomic;
     const int64_t N = S * k;
     const int64_t avg = N / std::max<int64_t>(E, 1);
-    pick_gemm(avg, pl.kind_up, pl.bm_up);
-    pick_gemm(avg, pl.kind_down, pl.bm_down);
+    pl.bm_up = pl.bm_down = pick_bm(avg);
     pl.n_mtiles_up = tiles_upper_bound(N, E, pl.bm_up);
     pl.n_mtiles_down = tiles_upper_bound(N, E, pl.bm_down);
     pl.bn_up = 128;
-    pl.bn_down = (pl.kind_down == kKindReg) ? 128 : 256;
+    pl.bn_down = (pl.bm_down == 32) ? 128 : 256;
     pl.n_ntiles_up = (int)((F + pl.bn_up - 1) / pl.bn_up);
     pl.n_ntiles_down = (int)((D + pl.bn_down - 1) / pl.bn_down);
     size_t off = 0;
@@ -202,15 +198,6 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k, bool ato
 static int grid_for(size_t n, int per_block) {
     const size_t b = (n + per_block - 1) / per_block;
     return (int)std::min<size_t>(std::max<size_t>(b, 1), 2048);
-}
-
-template <int BM, int BN, int WM, int WN, int MODE>
-static void launch_reg(const GemmParams &p0, hipStream_t stream) {
-    GemmParams p = p0;
-    p.n_ntiles = (p.N + BN - 1) / BN;  // equals the plan's count the order table was built for
-    const int blocks = p.n_mtiles * p.n_ntiles;
-    if (blocks == 0) return;
-    grouped_gemm_kernel<BM, BN, WM, WN, MODE><<<blocks, 256, 0, stream>>>(p);
 }
 
 static int device_cus() {
@@ -246,25 +233,29 @@ static void launch_pp_streamk(const GemmParams &p0, hipStream_t stream) {
 }
 
 template <int MODE>
-static void launch_gemm(int kind, int bm, const GemmParams &p, hipStream_t stream) {
+static void launch_gemm(int bm, const GemmParams &p, hipStream_t stream) {
     const int kid = MODE == kGateUp ? kKGateUp : kKDown;
     prof_begin(stream, kid);
-    if (kind == kKindPP) {
-        if constexpr (MODE == kGateUp) {
-            if (bm == 256) launch_pp_persistent<256, 128, MODE, 64, 2>(p, stream);
-            else launch_pp_persistent<192, 128, MODE, 32, 5>(p, stream);
-        } else if constexpr (MODE == kDown) {
-            if (bm == 256) launch_pp_streamk<256, 256, 32, 5>(p, stream);
-            else launch_pp_streamk<192, 256, 32, 5>(p, stream);
-        } else {
-            if (bm == 256) launch_pp_persistent<256, 256, MODE, 32, 5>(p, stream);
-            else launch_pp_persistent<192, 256, MODE, 32, 5>(p, stream);
+    if constexpr (MODE == kGateUp) {
+        switch (bm) {
+            case 256: launch_pp_persistent<256, 128, MODE, 64, 2>(p, stream); break;
+            case 192: launch_pp_persistent<192, 128, MODE, 32, 5>(p, stream); break;
+            case 64: launch_pp_persistent<64, 128, MODE, 64, 3>(p, stream); break;
+            default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;
+        }
+    } else if constexpr (MODE == kDown) {
+        switch (bm) {
+            case 256: launch_pp_streamk<256, 256, 32, 5>(p, stream); break;
+            case 192: launch_pp_streamk<192, 256, 32, 5>(p, stream); break;
+            case 64: launch_pp_streamk<64, 256, 64, 3>(p, stream); break;
+            default: launch_pp_streamk<32, 128, 64, 4>(p, stream); break;
         }
     } else {
         switch (bm) {
-            case 64: launch_reg<64, 128, 2, 2, MODE>(p, stream); break;
-            case 32: launch_reg<32, 128, 2, 2, MODE>(p, stream); break;
-            default: launch_reg<16, 128, 1, 4, MODE>(p, stream); break;
+            case 256: launch_pp_persistent<256, 256, MODE, 32, 5>(p, stream); break;
+            case 192: launch_pp_persistent<192, 256, MODE, 32, 5>(p, stream); break;
+            case 64: launch_pp_persistent<64, 256, MODE, 64, 3>(p, stream); break;
+            default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;
         }
     }
     prof_end(stream, kid);
@@ -313,7 +304,6 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.gate = topk_weights;
     p.topk = k;
     p.A_rows = S;
-    p.group_m = 8;
 
     // gate + up: A = gathered token rows of x, K = D, N = F
     p.tiles = tiles_up;
@@ -327,7 +317,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.N = F;
     p.K = D;
     p.valid_mtiles = valid_counts;
-    launch_gemm<kGateUp>(pl.kind_up, pl.bm_up, p, stream);
+    launch_gemm<kGateUp>(pl.bm_up, p, stream);
 
     // down + scatter-add (atomic) or per-route rows: A = h (slot order), K = F, N = D
     p.tiles = tiles_down;
@@ -341,13 +331,13 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.N = D;
     p.K = F;
     if (atomic) {
-        launch_gemm<kDown>(pl.kind_down, pl.bm_down, p, stream);
+        launch_gemm<kDown>(pl.bm_down, p, stream);
         prof_begin(stream, kKFinalize);
         acc_finalize_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
                                                                         reinterpret_cast<uint2 *>(out), n4);
         prof_end(stream, kKFinalize);
     } else {
-        launch_gemm<kDownRows>(pl.kind_down, pl.bm_down, p, stream);
+        launch_gemm<kDownRows>(pl.bm_down, p, stream);
         prof_begin(stream, kKCombine);
         combine_rows_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
                                                                         reinterpret_cast<uint2 *>(out), S, D / 4, k);

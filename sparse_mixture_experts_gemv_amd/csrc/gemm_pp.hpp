@@ -344,15 +344,6 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
     }
 }
 
-// One workgroup per output tile (full K).
-template <int BM, int BN, int MODE, int BK, int STAGES>
-__global__ __launch_bounds__(512) void grouped_gemm_pp_kernel(const GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[PPGeom<BM, BN, MODE, BK, STAGES>::SMEM];
-    int mt, nt;
-    if (!decode_tile(p, mt, nt)) return;
-    pp_tile<BM, BN, MODE, BK, STAGES>(p, smem, mt, nt, 0, p.K / BK);
-}
-
 // Persistent tile-granular form: one workgroup per CU walks the valid
 // blocks of the order table with stride gridDim.x (each XCD takes one
 // contiguous run of the order per round), so a tile's epilogue stores drain

@@ -31,8 +31,7 @@ constexpr int kOrderMaxNtiles = 1 << (32 - kOrderMtBits);
 
 struct FfnPlan {
     bool atomic;               // down GEMM: fp32 atomic scatter-add (else per-route rows + combine)
-    int kind_up, bm_up;        // gate+up GEMM: kernel kind and rows per M tile
-    int kind_down, bm_down;    // down GEMM
+    int bm_up, bm_down;        // rows per M tile of the gate+up and down GEMMs
     int bn_up, bn_down;        // columns per N tile
     int n_mtiles_up, n_mtiles_down;  // upper bounds on M tiles over all experts
     int n_ntiles_up, n_ntiles_down;

@@ -275,7 +275,6 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *w_gate, int S, int D,
     p.topk = 1;
     p.n_mtiles = (S + 127) / 128;
     p.n_ntiles = 1;
-    p.group_m = 1;
     const int blocks = p.n_mtiles * pl.nsplit;
     prof_begin(stream, kKRouteLogits);
     if (E <= 64) route_logits_kernel<64><<<blocks, 512, 0, stream>>>(p, pl.nsplit, partial);

@@ -1,7 +1,7 @@
 """moe_scatter_ffn_fwd and the whole forward pass on the GPU against the fp64 oracle.
 
 Small shapes are compared element by element over every token; they cover
-each M-tile size the launcher picks (16, 32, 64, 128 rows), ragged N tiles
+each M-tile height the launcher picks (32, 64, 192, 256 rows), ragged N tiles
 (F or D not a multiple of 128), ragged M tails and empty experts. The five
 configurations run at their full sizes with the launch configuration of the
 benchmark, and sampled tokens are checked one by one against the oracle.
@@ -34,11 +34,12 @@ def routing_for(p, seed):
     return torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
 
 
-SMALL = [  # (S, D, F, E, k): tile size picked from S*k/E
-    (1000, 192, 320, 8, 2),    # 250 rows/expert -> 128-row tiles, F ragged
+SMALL = [  # (S, D, F, E, k): tile height picked from S*k/E
+    (1000, 192, 320, 8, 2),    # 250 rows/expert -> 256-row tiles, F ragged
+    (600, 128, 192, 8, 2),     # 150 -> 192-row tiles
     (300, 128, 192, 8, 2),     # 75 -> 64-row tiles
     (200, 128, 256, 16, 2),    # 25 -> 32-row tiles
-    (40, 256, 128, 64, 8),     # 5 -> 16-row tiles, many empty experts
+    (40, 256, 128, 64, 8),     # 5 -> 32-row tiles, many empty experts
     (64, 2880, 2880, 128, 4),  # GPT-OSS widths: D and F = 45 * 64
     (33, 320, 192, 4, 1),      # k = 1
     (1, 64, 64, 8, 2),         # one token
