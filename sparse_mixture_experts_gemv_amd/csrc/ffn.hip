@@ -173,7 +173,10 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k, bool ato
     pl.n_mtiles_up = tiles_upper_bound(N, E, pl.bm_up);
     pl.n_mtiles_down = tiles_upper_bound(N, E, pl.bm_down);
     pl.bn_up = 128;
-    pl.bn_down = (pl.bm_down == 32) ? 128 : 256;
+    // per-route-rows down GEMM on 256-row tiles with a long reduction
+    // (F >= 8192): 256 x 128 tiles with 64-deep k-steps (three 48 KB stages)
+    pl.down_long_k = !atomic && pl.bm_down == 256 && F >= 8192;
+    pl.bn_down = (pl.bm_down == 32 || pl.down_long_k) ? 128 : 256;
     pl.n_ntiles_up = (int)((F + pl.bn_up - 1) / pl.bn_up);
     pl.n_ntiles_down = (int)((D + pl.bn_down - 1) / pl.bn_down);
     size_t off = 0;
@@ -233,7 +236,7 @@ static void launch_pp_streamk(const GemmParams &p0, hipStream_t stream) {
 }
 
 template <int MODE>
-static void launch_gemm(int bm, const GemmParams &p, hipStream_t stream) {
+static void launch_gemm(int bm, bool long_k, const GemmParams &p, hipStream_t stream) {
     const int kid = MODE == kGateUp ? kKGateUp : kKDown;
     prof_begin(stream, kid);
     if constexpr (MODE == kGateUp) {
@@ -252,7 +255,10 @@ static void launch_gemm(int bm, const GemmParams &p, hipStream_t stream) {
         }
     } else {
         switch (bm) {
-            case 256: launch_pp_persistent<256, 256, MODE, 32, 5>(p, stream); break;
+            case 256:
+                if (long_k) launch_pp_persistent<256, 128, MODE, 64, 3>(p, stream);
+                else launch_pp_persistent<256, 256, MODE, 32, 5>(p, stream);
+                break;
             case 192: launch_pp_persistent<192, 256, MODE, 32, 5>(p, stream); break;
             case 64: launch_pp_persistent<64, 256, MODE, 64, 3>(p, stream); break;
             default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;
@@ -317,7 +323,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.N = F;
     p.K = D;
     p.valid_mtiles = valid_counts;
-    launch_gemm<kGateUp>(pl.bm_up, p, stream);
+    launch_gemm<kGateUp>(pl.bm_up, false, p, stream);
 
     // down + scatter-add (atomic) or per-route rows: A = h (slot order), K = F, N = D
     p.tiles = tiles_down;
@@ -331,13 +337,13 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.N = D;
     p.K = F;
     if (atomic) {
-        launch_gemm<kDown>(pl.bm_down, p, stream);
+        launch_gemm<kDown>(pl.bm_down, false, p, stream);
         prof_begin(stream, kKFinalize);
         acc_finalize_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
                                                                         reinterpret_cast<uint2 *>(out), n4);
         prof_end(stream, kKFinalize);
     } else {
-        launch_gemm<kDownRows>(pl.bm_down, p, stream);
+        launch_gemm<kDownRows>(pl.bm_down, pl.down_long_k, p, stream);
         prof_begin(stream, kKCombine);
         combine_rows_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
                                                                         reinterpret_cast<uint2 *>(out), S, D / 4, k);

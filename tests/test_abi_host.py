@@ -109,7 +109,8 @@ def test_workspace_has_no_token_replication(lib):
     rows = lambda S, D, F, E, k: lib.moe_scatter_ffn_workspace_bytes(S, D, F, E, k)
     for (S, F, E, k) in [(4096, 14336, 8, 2), (4096, 2048, 256, 8), (8192, 2880, 128, 4)]:
         for D in (4096, 8192):
-            assert rows(S, D, F, E, k) - ws(S, D, F, E, k) == (S * k - S) * D * 4
+            # y [S*k, D] fp32 replaces acc [S, D] fp32 (plus a block-order table of at most a few KB)
+            assert 0 <= rows(S, D, F, E, k) - ws(S, D, F, E, k) - (S * k - S) * D * 4 < (1 << 20)
         d1, d2 = ws(S, 4096, F, E, k), ws(S, 8192, F, E, k)
         # growth with D: the fp32 accumulator plus a block-order table of a few KB,
         # nowhere near the S*k*D*2 bytes a token copy would add
