@@ -95,7 +95,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="mixtral", help="tiny | mixtral | gptoss | dsv3 | qwen2")
     ap.add_argument("--S", type=int, default=None, help="token count (default: the configuration's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -160,6 +160,16 @@ static int pick_bm(int64_t avg) {
     return 32;
 }
 
+// The down GEMM has few column tiles (D / 256), so its tile count is small
+// and the last round of the persistent grid can run half empty; its tile
+// height is chosen separately (measured on the five workloads): 192 rows for
+// long reductions (F >= 8192) and for ~100-190 rows per expert, 128 rows
+// with 64-deep k-steps for the other large batches.
+static int pick_bm_down(int64_t avg, int64_t F) {
+    if (avg >= 192) return F >= 8192 ? 192 : 128;
+    return pick_bm(avg);
+}
+
 static int tiles_upper_bound(int64_t N, int64_t E, int bm) {
     return (int)((N + std::min(E, N) * (bm - 1)) / bm);
 }
@@ -169,14 +179,12 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k, bool ato
     pl.atomic = atomic;
     const int64_t N = S * k;
     const int64_t avg = N / std::max<int64_t>(E, 1);
-    pl.bm_up = pl.bm_down = pick_bm(avg);
+    pl.bm_up = pick_bm(avg);
+    pl.bm_down = pick_bm_down(avg, F);
     pl.n_mtiles_up = tiles_upper_bound(N, E, pl.bm_up);
     pl.n_mtiles_down = tiles_upper_bound(N, E, pl.bm_down);
     pl.bn_up = 128;
-    // per-route-rows down GEMM on 256-row tiles with a long reduction
-    // (F >= 8192): 256 x 128 tiles with 64-deep k-steps (three 48 KB stages)
-    pl.down_long_k = !atomic && pl.bm_down == 256 && F >= 8192;
-    pl.bn_down = (pl.bm_down == 32 || pl.down_long_k) ? 128 : 256;
+    pl.bn_down = (pl.bm_down == 32) ? 128 : 256;
     pl.n_ntiles_up = (int)((F + pl.bn_up - 1) / pl.bn_up);
     pl.n_ntiles_down = (int)((D + pl.bn_down - 1) / pl.bn_down);
     size_t off = 0;
@@ -236,7 +244,7 @@ static void launch_pp_streamk(const GemmParams &p0, hipStream_t stream) {
 }
 
 template <int MODE>
-static void launch_gemm(int bm, bool long_k, const GemmParams &p, hipStream_t stream) {
+static void launch_gemm(int bm, const GemmParams &p, hipStream_t stream) {
     const int kid = MODE == kGateUp ? kKGateUp : kKDown;
     prof_begin(stream, kid);
     if constexpr (MODE == kGateUp) {
@@ -248,18 +256,15 @@ static void launch_gemm(int bm, bool long_k, const GemmParams &p, hipStream_t st
         }
     } else if constexpr (MODE == kDown) {
         switch (bm) {
-            case 256: launch_pp_streamk<256, 256, 32, 5>(p, stream); break;
             case 192: launch_pp_streamk<192, 256, 32, 5>(p, stream); break;
+            case 128: launch_pp_streamk<128, 256, 64, 3>(p, stream); break;
             case 64: launch_pp_streamk<64, 256, 64, 3>(p, stream); break;
             default: launch_pp_streamk<32, 128, 64, 4>(p, stream); break;
         }
     } else {
         switch (bm) {
-            case 256:
-                if (long_k) launch_pp_persistent<256, 128, MODE, 64, 3>(p, stream);
-                else launch_pp_persistent<256, 256, MODE, 32, 5>(p, stream);
-                break;
             case 192: launch_pp_persistent<192, 256, MODE, 32, 5>(p, stream); break;
+            case 128: launch_pp_persistent<128, 256, MODE, 64, 3>(p, stream); break;
             case 64: launch_pp_persistent<64, 256, MODE, 64, 3>(p, stream); break;
             default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;
         }
@@ -323,7 +328,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.N = F;
     p.K = D;
     p.valid_mtiles = valid_counts;
-    launch_gemm<kGateUp>(pl.bm_up, false, p, stream);
+    launch_gemm<kGateUp>(pl.bm_up, p, stream);
 
     // down + scatter-add (atomic) or per-route rows: A = h (slot order), K = F, N = D
     p.tiles = tiles_down;
@@ -337,13 +342,13 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.N = D;
     p.K = F;
     if (atomic) {
-        launch_gemm<kDown>(pl.bm_down, false, p, stream);
+        launch_gemm<kDown>(pl.bm_down, p, stream);
         prof_begin(stream, kKFinalize);
         acc_finalize_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
                                                                         reinterpret_cast<uint2 *>(out), n4);
         prof_end(stream, kKFinalize);
     } else {
-        launch_gemm<kDownRows>(pl.bm_down, pl.down_long_k, p, stream);
+        launch_gemm<kDownRows>(pl.bm_down, p, stream);
         prof_begin(stream, kKCombine);
         combine_rows_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
                                                                         reinterpret_cast<uint2 *>(out), S, D / 4, k);

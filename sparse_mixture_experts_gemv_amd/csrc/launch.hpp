@@ -31,7 +31,6 @@ constexpr int kOrderMaxNtiles = 1 << (32 - kOrderMtBits);
 
 struct FfnPlan {
     bool atomic;               // down GEMM: fp32 atomic scatter-add (else per-route rows + combine)
-    bool down_long_k;          // per-route-rows down GEMM with 256 x 128 tiles, 64-deep k-steps
     int bm_up, bm_down;        // rows per M tile of the gate+up and down GEMMs
     int bn_up, bn_down;        // columns per N tile
     int n_mtiles_up, n_mtiles_down;  // upper bounds on M tiles over all experts
