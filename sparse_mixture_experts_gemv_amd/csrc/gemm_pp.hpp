@@ -80,12 +80,14 @@ __device__ __forceinline__ void pp_wait_dma() {
 }
 
 // A tile rows are BK bf16 = CH chunks of 16 B (CH = 4 or 8). The chunk index
-// is XORed with a function of the row that keeps the 16 rows one
-// ds_read_b128 touches (one chunk each) in distinct banks, for LDS that
-// serves 128 or 256 bytes per cycle.
+// is XORed with a function of the row so that the fragment reads (16
+// consecutive rows, one chunk each, per 16-lane group) hit distinct banks;
+// both forms were checked with the LDS bank-conflict counter on gfx950 (the
+// 64-byte-row form r & 3 / (r >> 2) & 3 variants conflict, (r >> 1) & 3 does
+// not).
 template <int CH>
 __device__ __forceinline__ int pp_a_swz(int r) {
-    return (CH == 8) ? (((r >> 1) ^ ((r & 1) << 2)) & 7) : ((((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1));
+    return (CH == 8) ? (((r >> 1) ^ ((r & 1) << 2)) & 7) : ((r >> 1) & 3);
 }
 // B tile rows: BN bf16 in 32-byte segments (16 columns); segment XOR by k.
 template <int SEGS>
