@@ -162,11 +162,12 @@ static int pick_bm(int64_t avg) {
 
 // The down GEMM has few column tiles (D / 256), so its tile count is small
 // and the last round of the persistent grid can run half empty; its tile
-// height is chosen separately (measured on the five workloads): 192 rows for
-// long reductions (F >= 8192) and for ~100-190 rows per expert, 128 rows
-// with 64-deep k-steps for the other large batches.
-static int pick_bm_down(int64_t avg, int64_t F) {
-    if (avg >= 192) return F >= 8192 ? 192 : 128;
+// height is chosen separately (measured on the five workloads): 128 rows
+// with 64-deep k-steps for ~190-380 rows per expert, 192 rows above that and
+// for ~100-190 rows per expert.
+static int pick_bm_down(int64_t avg) {
+    if (avg >= 192 && avg < 384) return 128;
+    if (avg >= 96) return 192;
     return pick_bm(avg);
 }
 
@@ -180,7 +181,7 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k, bool ato
     const int64_t N = S * k;
     const int64_t avg = N / std::max<int64_t>(E, 1);
     pl.bm_up = pick_bm(avg);
-    pl.bm_down = pick_bm_down(avg, F);
+    pl.bm_down = pick_bm_down(avg);
     pl.n_mtiles_up = tiles_upper_bound(N, E, pl.bm_up);
     pl.n_mtiles_down = tiles_upper_bound(N, E, pl.bm_down);
     pl.bn_up = 128;
