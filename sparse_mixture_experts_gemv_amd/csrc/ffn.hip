@@ -227,12 +227,12 @@ static int device_cus() {
 // Gate+up and per-route-rows down GEMMs: one persistent workgroup per CU
 // walking whole tiles of the block order (plain-store epilogues, so tiles are
 // never split); a tile's epilogue overlaps the next tile's first loads.
-template <int BM, int BN, int MODE, int BK, int STAGES>
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES>
 static void launch_pp_persistent(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
     p.n_ntiles = (p.N + BN - 1) / BN;
     if (p.n_mtiles * p.n_ntiles == 0) return;
-    grouped_gemm_pp_persistent_kernel<BM, BN, MODE, BK, STAGES><<<device_cus(), 512, 0, stream>>>(p);
+    grouped_gemm_pp_persistent_kernel<BM, BN, MODE, BK, STAGES, STAGES_A><<<device_cus(), 512, 0, stream>>>(p);
 }
 
 // Stream-K down GEMM: one persistent workgroup per CU (160 KB of LDS each).
@@ -251,7 +251,7 @@ static void launch_gemm(int bm, const GemmParams &p, hipStream_t stream) {
     if constexpr (MODE == kGateUp) {
         switch (bm) {
             case 256: launch_pp_persistent<256, 128, MODE, 64, 2>(p, stream); break;
-            case 192: launch_pp_persistent<192, 128, MODE, 32, 5>(p, stream); break;
+            case 192: launch_pp_persistent<192, 128, MODE, 64, 3, 2>(p, stream); break;
             case 64: launch_pp_persistent<64, 128, MODE, 64, 3>(p, stream); break;
             default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;
         }
@@ -265,7 +265,7 @@ static void launch_gemm(int bm, const GemmParams &p, hipStream_t stream) {
     } else {
         switch (bm) {
             case 192: launch_pp_persistent<192, 256, MODE, 32, 5>(p, stream); break;
-            case 128: launch_pp_persistent<128, 256, MODE, 64, 3>(p, stream); break;
+            case 128: launch_pp_persistent<128, 256, MODE, 64, 4, 2>(p, stream); break;
             case 64: launch_pp_persistent<64, 256, MODE, 64, 3>(p, stream); break;
             default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;
         }

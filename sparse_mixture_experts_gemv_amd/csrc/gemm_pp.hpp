@@ -95,17 +95,22 @@ __device__ __forceinline__ int pp_b_swz(int k) {
     return (SEGS >= 8) ? ((k & 3) | (((k >> 3) & 1) << 2)) : (k & (SEGS - 1));
 }
 
-template <int BM, int BN, int MODE, int BK, int STAGES>
+// LDS: a ring of STAGES_A k-steps of A and a ring of STAGES k-steps of B.
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES>
 struct PPGeom {
     static constexpr int NB = (MODE == kGateUp) ? 2 : 1;
-    static constexpr int STAGE = BM * BK * 2 + NB * BK * BN * 2;
-    static constexpr int SMEM = STAGES * STAGE;
+    static constexpr int SMEM = STAGES_A * BM * BK * 2 + STAGES * NB * BK * BN * 2;
 };
 
 // One tile (mt, nt), k-steps [k_begin, k_end) of BK, epilogue included. All
 // 512 threads of the workgroup call it together; on return every LDS read of
 // the ring has completed, so the caller may start another tile.
-template <int BM, int BN, int MODE, int BK, int STAGES>
+//
+// The A (token rows) and B (weights) rings may have different depths: with
+// STAGES_A < STAGES the weights, which mostly come from HBM, are requested
+// STAGES - 1 steps ahead and the token rows, mostly L2 hits, STAGES_A - 1
+// steps ahead, within the same LDS budget.
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES>
 __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt, int nt, int k_begin, int k_end) {
     constexpr int NB = (MODE == kGateUp) ? 2 : 1;
     static_assert(BK == 32 || BK == 64, "K step");
@@ -120,7 +125,6 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
     constexpr int A_BYTES = BM * A_ROW;
     constexpr int B_ROW = BN * 2;
     constexpr int B_BYTES = BK * B_ROW;
-    constexpr int STAGE = A_BYTES + NB * B_BYTES;
     constexpr int A_INSTR = A_BYTES / 1024;
     constexpr int A_ROWS_PER_INSTR = 1024 / A_ROW;
     constexpr int B_INSTR_PER_MAT = B_BYTES / 1024;
@@ -132,8 +136,16 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
     constexpr int A_PER_WAVE = A_INSTR / 4;
     constexpr int B_PER_WAVE = B_INSTR / 4;
     constexpr int DMA_PER_WAVE = A_PER_WAVE + B_PER_WAVE;
-    static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS ring");
-    static_assert(DMA_PER_WAVE * (STAGES - 2) < 64, "vmcnt range");
+    static_assert(STAGES_A >= 2 && STAGES_A <= STAGES, "A ring no deeper than the B ring");
+    static_assert(STAGES_A * A_BYTES + STAGES * NB * B_BYTES <= 160 * 1024, "LDS rings");
+    constexpr int B_RING = STAGES_A * A_BYTES;  // byte offset of the B ring
+    // ops a group-0 wave may leave outstanding when the next step is needed:
+    // those issued after that step's A and after its B (steady state)
+    constexpr int WAIT_A = B_PER_WAVE + (STAGES_A - 2) * DMA_PER_WAVE;
+    constexpr int WAIT_B = (STAGES - 2) * DMA_PER_WAVE;
+    constexpr int WAIT_STEADY = WAIT_A < WAIT_B ? WAIT_A : WAIT_B;
+    constexpr int WAIT_FIRST = (STAGES_A - 2) * A_PER_WAVE + (STAGES - 2) * B_PER_WAVE;
+    static_assert(WAIT_FIRST < 64 && WAIT_STEADY < 64, "vmcnt range");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -193,17 +205,21 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
         }
     }
 
-#define SMOE_PP_ISSUE(KT)                                                                          \
+#define SMOE_PP_ISSUE_A(KT)                                                                        \
     {                                                                                              \
-        const uint32_t sbase = smem_addr + SMOE_SLOT(KT) * STAGE;                                  \
+        const uint32_t sbase = smem_addr + SMOE_SLOT_A(KT) * A_BYTES;                              \
         const uint32_t a_soff = (uint32_t)(KT) * (BK * 2);                                         \
         _Pragma("unroll") for (int i = 0; i < A_PER_WAVE; ++i)                                     \
             pp_dma16(a_rsrc, sbase + (wl + 4 * i) * 1024, a_voff[i], a_soff);                      \
+    }
+#define SMOE_PP_ISSUE_B(KT)                                                                        \
+    {                                                                                              \
+        const uint32_t sbase = smem_addr + B_RING + SMOE_SLOT_B(KT) * (NB * B_BYTES);              \
         const uint32_t b_soff = (uint32_t)(KT) * BK * ldb;                                         \
         _Pragma("unroll") for (int i = 0; i < B_PER_WAVE; ++i) {                                   \
             const int j = wl + 4 * i;                                                              \
-            pp_dma16((j / B_INSTR_PER_MAT) == 1 ? b_rsrc1 : b_rsrc0, sbase + A_BYTES + j * 1024,    \
-                     b_voff[i], b_soff);                                                           \
+            pp_dma16((j / B_INSTR_PER_MAT) == 1 ? b_rsrc1 : b_rsrc0, sbase + j * 1024, b_voff[i],  \
+                     b_soff);                                                                      \
         }                                                                                          \
     }
 
@@ -226,7 +242,7 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
             for (int h = 0; h < 2; ++h) {
                 const int k = kk * 32 + 8 * fg + 4 * h + (fr >> 2);
                 const int n = wn * WTN + j * 16 + 4 * (fr & 3);
-                b_rd[kk][j][h] = A_BYTES + k * B_ROW + (((n >> 4) ^ pp_b_swz<SEGS>(k)) << 5) + (n & 15) * 2;
+                b_rd[kk][j][h] = k * B_ROW + (((n >> 4) ^ pp_b_swz<SEGS>(k)) << 5) + (n & 15) * 2;
             }
 
     f32x4 acc[NB][MT][NT];
@@ -237,39 +253,48 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
 #pragma unroll
             for (int j = 0; j < NT; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // k-steps [k_begin, k_end); ring slot of step kt is (kt - k_begin) % STAGES
+    // k-steps [k_begin, k_end); ring slots of step kt are (kt - k_begin) % STAGES_A
+    // (A) and (kt - k_begin) % STAGES (B). Per step, group 0 issues A first,
+    // then B.
     const int KT = k_end;
-#define SMOE_SLOT(KT_) (((KT_) - k_begin) % STAGES)
+#define SMOE_SLOT_A(KT_) (((KT_) - k_begin) % STAGES_A)
+#define SMOE_SLOT_B(KT_) (((KT_) - k_begin) % STAGES)
     if (group == 0) {
 #pragma unroll
-        for (int st = 0; st < STAGES - 1; ++st)
-            if (k_begin + st < KT) SMOE_PP_ISSUE(k_begin + st);
-        if (KT - k_begin >= STAGES - 1) pp_wait_dma<DMA_PER_WAVE * (STAGES - 2)>();  // first step landed
+        for (int st = 0; st < STAGES - 1; ++st) {
+            if (st < STAGES_A - 1 && k_begin + st < KT) SMOE_PP_ISSUE_A(k_begin + st);
+            if (k_begin + st < KT) SMOE_PP_ISSUE_B(k_begin + st);
+        }
+        if (KT - k_begin >= STAGES - 1) pp_wait_dma<WAIT_FIRST>();  // first step landed
         else pp_wait_dma<0>();
     }
     pp_barrier();
     if (group == 1) pp_barrier();  // group 1 runs one phase behind
 
     for (int kt = k_begin; kt < KT; ++kt) {
-        // ---- read phase: refill the slot of step kt-1, then read step kt ----
-        if (group == 0 && kt + STAGES - 1 < KT) SMOE_PP_ISSUE(kt + STAGES - 1);
-        const char *s = smem + SMOE_SLOT(kt) * STAGE;
+        // ---- read phase: refill the slots of step kt-1, then read step kt ----
+        if (group == 0) {
+            if (kt + STAGES_A - 1 < KT) SMOE_PP_ISSUE_A(kt + STAGES_A - 1);
+            if (kt + STAGES - 1 < KT) SMOE_PP_ISSUE_B(kt + STAGES - 1);
+        }
+        const char *sa = smem + SMOE_SLOT_A(kt) * A_BYTES;
+        const char *sb = smem + B_RING + SMOE_SLOT_B(kt) * (NB * B_BYTES);
         uint4 af[KK][MT];
         uint4 bf[KK][NB][NT];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-            for (int i = 0; i < MT; ++i) af[kk][i] = *reinterpret_cast<const uint4 *>(s + a_rd[kk][i]);
+            for (int i = 0; i < MT; ++i) af[kk][i] = *reinterpret_cast<const uint4 *>(sa + a_rd[kk][i]);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
-                    const uint2 lo = pp_tr(s + b * B_BYTES + b_rd[kk][j][0]);
-                    const uint2 hi = pp_tr(s + b * B_BYTES + b_rd[kk][j][1]);
+                    const uint2 lo = pp_tr(sb + b * B_BYTES + b_rd[kk][j][0]);
+                    const uint2 hi = pp_tr(sb + b * B_BYTES + b_rd[kk][j][1]);
                     bf[kk][b][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 }
         }
-        // reads complete before the barrier: after it the slot may be refilled
+        // reads complete before the barrier: after it the slots may be refilled
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         pp_barrier();
         // ---- MFMA phase ----
@@ -285,14 +310,16 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
                         acc[b][i][j] = mfma_16x16x32(af[kk][i], bf[kk][b][j], acc[b][i][j]);
         __builtin_amdgcn_s_setprio(0);
         if (group == 0) {  // step kt+1 must have landed before the barrier that opens it
-            if (kt + STAGES - 1 < KT) pp_wait_dma<DMA_PER_WAVE * (STAGES - 2)>();
+            if (kt + STAGES - 1 < KT) pp_wait_dma<WAIT_STEADY>();
             else pp_wait_dma<0>();
         }
         pp_barrier();
     }
     if (group == 0) pp_barrier();
-#undef SMOE_PP_ISSUE
-#undef SMOE_SLOT
+#undef SMOE_PP_ISSUE_A
+#undef SMOE_PP_ISSUE_B
+#undef SMOE_SLOT_A
+#undef SMOE_SLOT_B
 
     // ---- epilogue (C layout: lane holds column lane % 16, rows 4 (lane / 16) + r) ----
     const int col_in_tile = lane & 15;
@@ -304,7 +331,7 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
             const int row = wm * WTM + i * 16 + row_grp + r;
             const int slot = row0 + row;
             if (slot >= row1) continue;
-            if (MODE == kGateUp) {
+            if constexpr (MODE == kGateUp) {
                 uint16_t *h = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * N + n0;
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
@@ -315,7 +342,7 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
                         h[col] = f32_to_bf16_bits(sg * u);
                     }
                 }
-            } else if (MODE == kDown) {
+            } else if constexpr (MODE == kDown) {
                 const int f = p.slot_src[slot];
                 const int tok = f / p.topk;
                 const float w = p.gate[f];
@@ -325,7 +352,7 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
                     const int col = wn * WTN + j * 16 + col_in_tile;
                     if (n0 + col < N) atomicAdd(accp + col, w * acc[0][i][j][r]);
                 }
-            } else if (MODE == kDownRows) {
+            } else if constexpr (MODE == kDownRows) {
                 const int f = p.slot_src[slot];
                 const float w = p.gate[f];
                 float *yp = reinterpret_cast<float *>(p.C) + (size_t)f * N + n0;
@@ -350,15 +377,15 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
 // blocks of the order table with stride gridDim.x (each XCD takes one
 // contiguous run of the order per round), so a tile's epilogue stores drain
 // while the same workgroup already streams its next tile.
-template <int BM, int BN, int MODE, int BK, int STAGES>
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES>
 __global__ __launch_bounds__(512) void grouped_gemm_pp_persistent_kernel(const GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[PPGeom<BM, BN, MODE, BK, STAGES>::SMEM];
+    __shared__ __attribute__((aligned(1024))) char smem[PPGeom<BM, BN, MODE, BK, STAGES, STAGES_A>::SMEM];
     const int total = (*p.valid_mtiles) * p.n_ntiles;
     const int G = gridDim.x;
     for (int L = xcd_remap(blockIdx.x, G); L < total; L += G) {
         const uint32_t v = p.order[L];
         const int mt = (int)(v & kOrderMtMask), nt = (int)(v >> kOrderMtBits);
-        if (mt < p.n_mtiles) pp_tile<BM, BN, MODE, BK, STAGES>(p, smem, mt, nt, 0, p.K / BK);
+        if (mt < p.n_mtiles) pp_tile<BM, BN, MODE, BK, STAGES, STAGES_A>(p, smem, mt, nt, 0, p.K / BK);
     }
 }
 
