@@ -227,12 +227,13 @@ static int device_cus() {
 // Gate+up and per-route-rows down GEMMs: one persistent workgroup per CU
 // walking whole tiles of the block order (plain-store epilogues, so tiles are
 // never split); a tile's epilogue overlaps the next tile's first loads.
-template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES>
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool SKIP_ROWS = false>
 static void launch_pp_persistent(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
     p.n_ntiles = (p.N + BN - 1) / BN;
     if (p.n_mtiles * p.n_ntiles == 0) return;
-    grouped_gemm_pp_persistent_kernel<BM, BN, MODE, BK, STAGES, STAGES_A><<<device_cus(), 512, 0, stream>>>(p);
+    grouped_gemm_pp_persistent_kernel<BM, BN, MODE, BK, STAGES, STAGES_A, SKIP_ROWS>
+        <<<device_cus(), 512, 0, stream>>>(p);
 }
 
 // Stream-K down GEMM: one persistent workgroup per CU (160 KB of LDS each).
@@ -244,14 +245,17 @@ static void launch_pp_streamk(const GemmParams &p0, hipStream_t stream) {
     grouped_gemm_pp_streamk_kernel<BM, BN, BK, STAGES><<<device_cus(), 512, 0, stream>>>(p);
 }
 
+// avg = mean rows per expert. Where it is below the tile height (experts of
+// ~100-190 rows under 192-row tiles) most tiles are short, so those launches
+// skip the MFMAs and row loads of missing rows.
 template <int MODE>
-static void launch_gemm(int bm, const GemmParams &p, hipStream_t stream) {
+static void launch_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t stream) {
     const int kid = MODE == kGateUp ? kKGateUp : kKDown;
     prof_begin(stream, kid);
     if constexpr (MODE == kGateUp) {
         switch (bm) {
             case 256: launch_pp_persistent<256, 128, MODE, 64, 2>(p, stream); break;
-            case 192: launch_pp_persistent<192, 128, MODE, 64, 3, 2>(p, stream); break;
+            case 192: launch_pp_persistent<192, 128, MODE, 64, 3, 2, true>(p, stream); break;
             case 64: launch_pp_persistent<64, 128, MODE, 64, 3>(p, stream); break;
             default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;
         }
@@ -264,7 +268,10 @@ static void launch_gemm(int bm, const GemmParams &p, hipStream_t stream) {
         }
     } else {
         switch (bm) {
-            case 192: launch_pp_persistent<192, 256, MODE, 32, 5>(p, stream); break;
+            case 192:
+                if (avg < 192) launch_pp_persistent<192, 256, MODE, 64, 3, 2, true>(p, stream);
+                else launch_pp_persistent<192, 256, MODE, 32, 5>(p, stream);
+                break;
             case 128: launch_pp_persistent<128, 256, MODE, 64, 4, 2>(p, stream); break;
             case 64: launch_pp_persistent<64, 256, MODE, 64, 3>(p, stream); break;
             default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;
@@ -329,7 +336,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.N = F;
     p.K = D;
     p.valid_mtiles = valid_counts;
-    launch_gemm<kGateUp>(pl.bm_up, p, stream);
+    launch_gemm<kGateUp>(pl.bm_up, (int64_t)N / E, p, stream);
 
     // down + scatter-add (atomic) or per-route rows: A = h (slot order), K = F, N = D
     p.tiles = tiles_down;
@@ -343,13 +350,13 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.N = D;
     p.K = F;
     if (atomic) {
-        launch_gemm<kDown>(pl.bm_down, p, stream);
+        launch_gemm<kDown>(pl.bm_down, (int64_t)N / E, p, stream);
         prof_begin(stream, kKFinalize);
         acc_finalize_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
                                                                         reinterpret_cast<uint2 *>(out), n4);
         prof_end(stream, kKFinalize);
     } else {
-        launch_gemm<kDownRows>(pl.bm_down, p, stream);
+        launch_gemm<kDownRows>(pl.bm_down, (int64_t)N / E, p, stream);
         prof_begin(stream, kKCombine);
         combine_rows_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
                                                                         reinterpret_cast<uint2 *>(out), S, D / 4, k);

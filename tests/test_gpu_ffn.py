@@ -69,6 +69,27 @@ def test_ffn_skewed_single_expert(oracle_lib, atomic):
     assert_close(got, ref, f"two hot experts {'atomic' if atomic else 'rows'}", configured=False)
 
 
+@pytest.mark.parametrize("atomic", [False, True], ids=["rows", "atomic"])
+def test_ffn_short_tiles_row_edges(oracle_lib, atomic):
+    """Experts whose row counts straddle every edge of the short-tile path of
+    the 192-row tiles (mean 120 rows per expert): 8-row load groups (7, 8,
+    9), 16-row MFMA blocks (15, 16, 17), wave row groups (31, 33, 96, 128,
+    160), a full tile (192), one row past it (193) and a many-tile expert."""
+    S, k, E = 960, 2, 16
+    counts = [1, 7, 8, 9, 15, 16, 17, 31, 33, 96, 128, 160, 191, 192, 193]
+    counts.append(S * k - sum(counts))
+    assert max(counts) <= S
+    flat = np.repeat(np.arange(E, dtype=np.int32), counts)   # sorted by expert
+    ids = np.stack([flat[:S], flat[S:]], axis=1)             # distinct per token since every count <= S
+    assert np.all(ids[:, 0] != ids[:, 1])
+    cfg = wl.MoEConfig("edges", 62, S, 256, 384, E, k, None)
+    p = make_problem(cfg)
+    w = np.random.default_rng(1).dirichlet(np.ones(k), size=S).astype(np.float32)
+    got = gpu_ffn(p, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), atomic)
+    ref = oracle_ffn_rows(oracle_lib, p, ids, w, np.arange(S))
+    assert_close(got, ref, f"short-tile row edges {'atomic' if atomic else 'rows'}", configured=False)
+
+
 def test_ffn_rows_combine_is_bitwise_reproducible():
     """The ordered combine gives the same bits on every call, also for k = 8."""
     cfg = wl.MoEConfig("repro", 62, 500, 256, 192, 64, 8, None)
