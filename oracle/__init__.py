@@ -44,6 +44,12 @@ class Oracle:
         L.oracle_ffn_tokens.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P,
                                         ctypes.c_int]
         L.oracle_ffn_tokens.restype = ctypes.c_int
+        L.oracle_parallel_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_int,
+                                             ctypes.c_int, _P]
+        L.oracle_parallel_linear.restype = ctypes.c_int
+        L.oracle_parallel_linear_bwd.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_int,
+                                                 ctypes.c_int, _P, _P, _P]
+        L.oracle_parallel_linear_bwd.restype = ctypes.c_int
 
     @staticmethod
     def _ptr(a: Optional[np.ndarray]):
@@ -102,6 +108,44 @@ class Oracle:
         if st:
             raise ValueError(f"oracle_ffn_tokens status {st}")
         return out
+
+    @staticmethod
+    def _pl_args(x_bits, w_bits, ids, gates, grouped_in):
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        w_bits = np.ascontiguousarray(w_bits, dtype=np.uint16)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        S, k = ids.shape
+        E, D_in, D_out = w_bits.shape
+        assert x_bits.shape == ((S * k if grouped_in else S), D_in)
+        if gates is not None:
+            gates = np.ascontiguousarray(gates, dtype=np.float64).reshape(S * k)
+        return x_bits, w_bits, ids, gates, S, k, E, D_in, D_out
+
+    def parallel_linear(self, x_bits, w_bits, ids, gates=None, grouped_in=False, grouped_out=False):
+        """ParallelLinear(X, W, I, G) -> f64 [S*k or S, D_out] (grouped rows are in slot order)."""
+        x_bits, w_bits, ids, gates, S, k, E, D_in, D_out = self._pl_args(x_bits, w_bits, ids, gates, grouped_in)
+        y = np.zeros(((S * k if grouped_out else S), D_out), dtype=np.float64)
+        st = self.lib.oracle_parallel_linear(self._ptr(x_bits), self._ptr(w_bits), self._ptr(gates), self._ptr(ids),
+                                             S, k, D_in, D_out, E, int(grouped_in), int(grouped_out), self._ptr(y))
+        if st:
+            raise ValueError(f"oracle_parallel_linear status {st}")
+        return y
+
+    def parallel_linear_bwd(self, x_bits, w_bits, ids, dy_bits, gates=None, grouped_in=False, grouped_out=False):
+        """Backward of ParallelLinear -> (dx f64, dw f64 [E, D_in, D_out], dg f64 [S, k])."""
+        x_bits, w_bits, ids, gates, S, k, E, D_in, D_out = self._pl_args(x_bits, w_bits, ids, gates, grouped_in)
+        dy_bits = np.ascontiguousarray(dy_bits, dtype=np.uint16)
+        assert dy_bits.shape == ((S * k if grouped_out else S), D_out)
+        dx = np.zeros(((S * k if grouped_in else S), D_in), dtype=np.float64)
+        dw = np.zeros((E, D_in, D_out), dtype=np.float64)
+        dg = np.zeros((S, k), dtype=np.float64)
+        st = self.lib.oracle_parallel_linear_bwd(self._ptr(x_bits), self._ptr(w_bits), self._ptr(gates),
+                                                 self._ptr(ids), self._ptr(dy_bits), S, k, D_in, D_out, E,
+                                                 int(grouped_in), int(grouped_out), self._ptr(dx), self._ptr(dw),
+                                                 self._ptr(dg))
+        if st:
+            raise ValueError(f"oracle_parallel_linear_bwd status {st}")
+        return dx, dw, dg
 
     def layer(self, x_bits, wg_bits, w1_bits, w3_bits, w2_bits, k, tokens=None, nthreads=None):
         """Route, map and FFN of the whole forward (map returned for inspection)."""

@@ -248,3 +248,143 @@ int oracle_ffn_tokens(const uint16_t *x, const uint16_t *w1, const uint16_t *w3,
     free(jobs); free(th);
     return st;
 }
+
+/* ------------------------------------------------------ parallel linear -- */
+
+/*
+ * ParallelLinear(X, W, I, G) (ScatterMoE Guide, "1. The Anatomy of
+ * ParallelLinear" and the figure "The ParallelLinear Core Abstraction"):
+ * the routes f = t*k + j (token t, expert e = ids[f], gate g_f) are sorted
+ * by expert into slots r (the map above). For every route
+ *     z_f = g_f * in(f) W[e]                          (length D_out)
+ * where in(f) = x[r] (grouped input: x holds S*k rows in slot order) or
+ * x[t] (scattered input: x holds S token rows). The output is
+ *     y[r] = z_f          (grouped output, S*k rows in slot order) or
+ *     y[t] = sum_j z_f    (scattered output, S token rows, summed j = 0..k-1).
+ * gates == NULL means g_f = 1. W is [E, D_in, D_out] (bf16 bits); y is fp64.
+ */
+static int pl_map(const int32_t *ids, int64_t S, int64_t k, int64_t E, int32_t **rows_out) {
+    int64_t n = S * k;
+    int32_t *counts = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    int32_t *offsets = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    int32_t *src = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    if (!counts || !offsets || !rows || !src) { free(counts); free(offsets); free(rows); free(src); return 2; }
+    int st = oracle_sparse_map(ids, S, k, E, counts, offsets, rows, src);
+    free(counts); free(offsets); free(src);
+    if (st) { free(rows); return st; }
+    *rows_out = rows;
+    return 0;
+}
+
+/* z = in W[e]: in [D_in] bf16 bits, we [D_in, D_out] bf16 bits, z [D_out] fp64 */
+static void row_times_w(const uint16_t *in, const uint16_t *we, int64_t D_in, int64_t D_out, double *z) {
+    for (int64_t n = 0; n < D_out; ++n) z[n] = 0.0;
+    for (int64_t d = 0; d < D_in; ++d) {
+        double v = bf16_to_double(in[d]);
+        const uint16_t *wr = we + d * D_out;
+        for (int64_t n = 0; n < D_out; ++n) z[n] += v * bf16_to_double(wr[n]);
+    }
+}
+
+/* c = dy W[e]^T: dy [D_out] bf16 bits, c [D_in] fp64 (c[d] = sum_n dy[n] W[e][d, n]) */
+static void row_times_wt(const uint16_t *dy, const uint16_t *we, int64_t D_in, int64_t D_out, double *c) {
+    for (int64_t d = 0; d < D_in; ++d) {
+        const uint16_t *wr = we + d * D_out;
+        double s = 0.0;
+        for (int64_t n = 0; n < D_out; ++n) s += bf16_to_double(dy[n]) * bf16_to_double(wr[n]);
+        c[d] = s;
+    }
+}
+
+int oracle_parallel_linear(const uint16_t *x, const uint16_t *w, const double *gates, const int32_t *ids,
+                           int64_t S, int64_t k, int64_t D_in, int64_t D_out, int64_t E, int grouped_in,
+                           int grouped_out, double *y) {
+    if (S < 0 || k < 1 || D_in < 1 || D_out < 1 || E < 1) return 1;
+    int32_t *rows = NULL;
+    int st = pl_map(ids, S, k, E, &rows);
+    if (st) return st;
+    double *z = (double *)malloc(sizeof(double) * (size_t)D_out);
+    if (!z) { free(rows); return 2; }
+    int64_t n_out = grouped_out ? S * k : S;
+    for (int64_t i = 0; i < n_out * D_out; ++i) y[i] = 0.0;
+    for (int64_t t = 0; t < S; ++t) {
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t f = t * k + j, r = rows[f], e = ids[f];
+            const uint16_t *in = grouped_in ? x + r * D_in : x + t * D_in;
+            row_times_w(in, w + e * D_in * D_out, D_in, D_out, z);
+            double g = gates ? gates[f] : 1.0;
+            double *o = grouped_out ? y + r * D_out : y + t * D_out;
+            for (int64_t n = 0; n < D_out; ++n) o[n] += g * z[n];
+        }
+    }
+    free(z); free(rows);
+    return 0;
+}
+
+/*
+ * Backward of ParallelLinear (ScatterMoE Guide, "3. Fused Backward Pass
+ * Dynamics"): with dy_f = dy[r] (grouped output) or dy[t] (scattered output),
+ *     dx:  c_f = g_f * dy_f W[e]^T;  dx[r] = c_f (grouped input) or
+ *          dx[t] = sum_j c_f (scattered input, j = 0..k-1)
+ *     dw:  dw[e] = sum over the slots r of expert e, ascending, of
+ *          g_f * in(f)^T dy_f                        ([D_in, D_out])
+ *     dg:  dg[f] = <dy_f, in(f) W[e]>               (the router coefficient's
+ *          gradient; needs no gates)
+ * Any of dx, dw, dg may be NULL. All outputs fp64; dw is [E, D_in, D_out]
+ * and is zero for an expert with no routes.
+ */
+int oracle_parallel_linear_bwd(const uint16_t *x, const uint16_t *w, const double *gates, const int32_t *ids,
+                               const uint16_t *dy, int64_t S, int64_t k, int64_t D_in, int64_t D_out, int64_t E,
+                               int grouped_in, int grouped_out, double *dx, double *dw, double *dg) {
+    if (S < 0 || k < 1 || D_in < 1 || D_out < 1 || E < 1) return 1;
+    int32_t *rows = NULL;
+    int st = pl_map(ids, S, k, E, &rows);
+    if (st) return st;
+    int64_t n = S * k;
+    int32_t *src = (int32_t *)calloc((size_t)(n > 0 ? n : 1), sizeof(int32_t));
+    double *c = (double *)malloc(sizeof(double) * (size_t)(D_in > D_out ? D_in : D_out));
+    if (!src || !c) { free(rows); free(src); free(c); return 2; }
+    for (int64_t f = 0; f < n; ++f) src[rows[f]] = (int32_t)f;
+    if (dx) {
+        int64_t n_in = grouped_in ? n : S;
+        for (int64_t i = 0; i < n_in * D_in; ++i) dx[i] = 0.0;
+        for (int64_t t = 0; t < S; ++t) {
+            for (int64_t j = 0; j < k; ++j) {
+                int64_t f = t * k + j, r = rows[f], e = ids[f];
+                const uint16_t *d = grouped_out ? dy + r * D_out : dy + t * D_out;
+                row_times_wt(d, w + e * D_in * D_out, D_in, D_out, c);
+                double g = gates ? gates[f] : 1.0;
+                double *o = grouped_in ? dx + r * D_in : dx + t * D_in;
+                for (int64_t i = 0; i < D_in; ++i) o[i] += g * c[i];
+            }
+        }
+    }
+    if (dw) {
+        for (int64_t i = 0; i < E * D_in * D_out; ++i) dw[i] = 0.0;
+        for (int64_t r = 0; r < n; ++r) {
+            int64_t f = src[r], t = f / k, e = ids[f];
+            const uint16_t *in = grouped_in ? x + r * D_in : x + t * D_in;
+            const uint16_t *d = grouped_out ? dy + r * D_out : dy + t * D_out;
+            double g = gates ? gates[f] : 1.0;
+            double *we = dw + e * D_in * D_out;
+            for (int64_t a = 0; a < D_in; ++a) {
+                double xa = g * bf16_to_double(in[a]);
+                for (int64_t b = 0; b < D_out; ++b) we[a * D_out + b] += xa * bf16_to_double(d[b]);
+            }
+        }
+    }
+    if (dg) {
+        for (int64_t f = 0; f < n; ++f) {
+            int64_t r = rows[f], t = f / k, e = ids[f];
+            const uint16_t *in = grouped_in ? x + r * D_in : x + t * D_in;
+            const uint16_t *d = grouped_out ? dy + r * D_out : dy + t * D_out;
+            row_times_w(in, w + e * D_in * D_out, D_in, D_out, c);
+            double s = 0.0;
+            for (int64_t b = 0; b < D_out; ++b) s += bf16_to_double(d[b]) * c[b];
+            dg[f] = s;
+        }
+    }
+    free(rows); free(src); free(c);
+    return 0;
+}

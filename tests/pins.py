@@ -219,5 +219,115 @@ def pin_invariances(o, seed=9):
     assert np.array_equal(o.ffn(p["x"], p["w1"], p["w3"], p["w2"], ids, w, tokens=tok), base[tok]), "token subset"
 
 
+# ------------------------------------------------------- parallel linear --
+
+PL_MODES = [(False, False), (False, True), (True, False), (True, True)]  # (grouped_in, grouped_out)
+
+
+def pl_problem(S=40, k=2, D_in=48, D_out=40, E=8, seed=0, grouped_in=False, grouped_out=False, skew=None):
+    """Random ParallelLinear problem (bf16 bit arrays); x / dy hold S*k slot rows when grouped."""
+    rng = np.random.default_rng(seed)
+    ids = wl.gen_random_ids(S, k, E, seed=seed + 11, skew=skew)
+    x = bf16_bits_from_f32(rng.standard_normal(((S * k if grouped_in else S), D_in)))
+    w = bf16_bits_from_f32(rng.standard_normal((E, D_in, D_out)) * D_in ** -0.5)
+    g = rng.dirichlet(np.ones(k), size=S)
+    dy = bf16_bits_from_f32(rng.standard_normal(((S * k if grouped_out else S), D_out)))
+    return dict(x=x, w=w, ids=ids, g=g, dy=dy)
+
+
+def dense_gate_matrix(ids, g, E):
+    G = np.zeros((ids.shape[0], E))
+    for j in range(ids.shape[1]):
+        G[np.arange(ids.shape[0]), ids[:, j]] += g[:, j]
+    return G
+
+
+def library_slots(ids):
+    """(slot_src, sparse_rows) from numpy's stable argsort of the flat expert ids."""
+    src = np.argsort(ids.reshape(-1), kind="stable")
+    rows = np.empty_like(src)
+    rows[src] = np.arange(src.size)
+    return src, rows
+
+
+def pin_parallel_linear_dense_mask(o, seed=20):
+    """Scattered in and out: y = sum_e G[:, e] * (X W_e), every expert on every token masked by the
+    dense gate matrix (gates given, and gates absent = indicator matrix)."""
+    for (S, k, E) in [(40, 2, 8), (24, 4, 4), (30, 1, 16)]:
+        p = pl_problem(S=S, k=k, E=E, seed=seed + E)
+        X, W = bits_to_f64(p["x"]), bits_to_f64(p["w"])
+        for gates in (p["g"], None):
+            y = o.parallel_linear(p["x"], p["w"], p["ids"], gates)
+            G = dense_gate_matrix(p["ids"], p["g"] if gates is not None else np.ones_like(p["g"]), E)
+            ref = sum(G[:, e:e + 1] * (X @ W[e]) for e in range(E))
+            assert rel_err(y, ref) < 1e-12, f"dense mask S={S} k={k} E={E}"
+
+
+def pin_parallel_linear_modes(o, seed=21):
+    """Grouped layouts are slot-order permutations (library argsort) of the scattered ones: grouped
+    output rows taken back to route order and summed over j give the scattered output; grouped
+    input rows gathered by slot give the scattered-input result bit for bit."""
+    p = pl_problem(S=36, k=3, E=8, seed=seed, skew=1.2)
+    src, rows = library_slots(p["ids"])
+    S, k = p["ids"].shape
+    ys = o.parallel_linear(p["x"], p["w"], p["ids"], p["g"])
+    yg = o.parallel_linear(p["x"], p["w"], p["ids"], p["g"], grouped_out=True)
+    assert rel_err(yg[rows].reshape(S, k, -1).sum(1), ys) < 1e-13, "grouped output = permuted routes"
+    xg = p["x"][src // k]  # slot r holds its token's row
+    assert np.array_equal(o.parallel_linear(xg, p["w"], p["ids"], p["g"], grouped_in=True), ys), "grouped input"
+    assert np.array_equal(o.parallel_linear(xg, p["w"], p["ids"], p["g"], grouped_in=True, grouped_out=True), yg)
+
+
+def pin_parallel_linear_single_expert(o, seed=22):
+    """E = 1, k = 1, no gates: every mode is the plain product X W (numpy matmul)."""
+    for gi, go in PL_MODES:
+        p = pl_problem(S=33, k=1, D_in=40, D_out=56, E=1, seed=seed, grouped_in=gi, grouped_out=go)
+        y = o.parallel_linear(p["x"], p["w"], p["ids"], None, gi, go)
+        assert rel_err(y, bits_to_f64(p["x"]) @ bits_to_f64(p["w"][0])) < 1e-13
+
+
+def pin_parallel_linear_bwd_adjoint(o, seed=23):
+    """y is linear in x, in W and in g, so with s = <dy, y>: <dx, x> = s, sum_e <dw_e, W_e> = s and
+    sum_f g_f dg_f = s (the adjoint identities), in every grouping mode, skewed routing included."""
+    for gi, go in PL_MODES:
+        for skew in (None, 1.2):
+            p = pl_problem(S=30, k=2, E=8, seed=seed + 2 * gi + go, grouped_in=gi, grouped_out=go, skew=skew)
+            y = o.parallel_linear(p["x"], p["w"], p["ids"], p["g"], gi, go)
+            dx, dw, dg = o.parallel_linear_bwd(p["x"], p["w"], p["ids"], p["dy"], p["g"], gi, go)
+            s = float(np.sum(bits_to_f64(p["dy"]) * y))
+            tol = 1e-10 * float(np.sum(np.abs(bits_to_f64(p["dy"]) * y)))
+            assert abs(float(np.sum(dx * bits_to_f64(p["x"]))) - s) < tol, f"<dx, x> mode {gi}{go}"
+            assert abs(float(np.sum(dw * bits_to_f64(p["w"]))) - s) < tol, f"<dw, W> mode {gi}{go}"
+            assert abs(float(np.sum(dg * p["g"])) - s) < tol, f"<dg, g> mode {gi}{go}"
+
+
+def pin_parallel_linear_bwd_dense(o, seed=24):
+    """Scattered in and out: dx = sum_e G[:, e] * (dY W_e^T), dw_e = (G[:, e] * X)^T dY and
+    dg[t, j] = <dY[t], X[t] W_{ids[t, j]}> by dense numpy products; E = 1, k = 1 reduces to
+    dx = dY W^T, dw = X^T dY in every mode; an expert with no routes gets dw = 0."""
+    p = pl_problem(S=40, k=2, E=8, seed=seed)
+    X, W, dY = bits_to_f64(p["x"]), bits_to_f64(p["w"]), bits_to_f64(p["dy"])
+    ids = p["ids"].copy()
+    ids[ids == 5] = 6  # expert 5 gets no routes (ids stay distinct per token unless 5 and 6 met)
+    ids[:, 1] = np.where(ids[:, 1] == ids[:, 0], (ids[:, 0] + 1) % 5, ids[:, 1])
+    assert np.all(ids[:, 0] != ids[:, 1]) and not np.any(ids == 5)
+    dx, dw, dg = o.parallel_linear_bwd(p["x"], p["w"], ids, p["dy"], p["g"])
+    G = dense_gate_matrix(ids, p["g"], 8)
+    assert rel_err(dx, sum(G[:, e:e + 1] * (dY @ W[e].T) for e in range(8))) < 1e-12, "dense dx"
+    for e in range(8):
+        ref = (G[:, e:e + 1] * X).T @ dY
+        assert (np.all(dw[e] == 0) if e == 5 else rel_err(dw[e], ref) < 1e-12), f"dense dw[{e}]"
+    P = np.stack([X @ W[e] for e in range(8)])  # every expert on every token [E, S, D_out]
+    ref_dg = np.stack([np.sum(dY * P[ids[:, j], np.arange(40)], axis=1) for j in range(2)], axis=1)
+    assert rel_err(dg, ref_dg) < 1e-12, "dense dg"
+    for gi, go in PL_MODES:
+        q = pl_problem(S=27, k=1, D_in=40, D_out=32, E=1, seed=seed + 1, grouped_in=gi, grouped_out=go)
+        dx1, dw1, _ = o.parallel_linear_bwd(q["x"], q["w"], q["ids"], q["dy"], None, gi, go)
+        assert rel_err(dx1, bits_to_f64(q["dy"]) @ bits_to_f64(q["w"][0]).T) < 1e-13, f"E=1 dx {gi}{go}"
+        assert rel_err(dw1[0], bits_to_f64(q["x"]).T @ bits_to_f64(q["dy"])) < 1e-13, f"E=1 dw {gi}{go}"
+
+
 ALL_PINS = [pin_router_library, pin_router_full_softmax, pin_router_ties, pin_router_given_ids,
-            pin_sparse_map, pin_brute_force, pin_dense_single_expert, pin_shared_experts, pin_invariances]
+            pin_sparse_map, pin_brute_force, pin_dense_single_expert, pin_shared_experts, pin_invariances,
+            pin_parallel_linear_dense_mask, pin_parallel_linear_modes, pin_parallel_linear_single_expert,
+            pin_parallel_linear_bwd_adjoint, pin_parallel_linear_bwd_dense]

@@ -33,6 +33,24 @@ MUTANTS = {
     "offsets_off_by_one": ("offsets[e + 1] = offsets[e] + counts[e];",
                            "offsets[e + 1] = offsets[e] + counts[e] - (e == 0 && counts[0] > 0);"),
     "x_row_of_wrong_token": ("expert_row(jb->x + s * D,", "expert_row(jb->x + (s > 0 && j == 1 ? s - 1 : s) * D,"),
+    # ParallelLinear forward and backward
+    "pl_gate_dropped": ("for (int64_t n = 0; n < D_out; ++n) o[n] += g * z[n];",
+                        "for (int64_t n = 0; n < D_out; ++n) o[n] += z[n];"),
+    "pl_grouped_out_in_route_order": ("double *o = grouped_out ? y + r * D_out : y + t * D_out;",
+                                      "double *o = grouped_out ? y + f * D_out : y + t * D_out;"),
+    "pl_w_row_off_by_one": ("const uint16_t *wr = we + d * D_out;\n        for (int64_t n = 0; n < D_out; ++n) z[n]",
+                            "const uint16_t *wr = we + ((d + 1) % D_in) * D_out;\n        for (int64_t n = 0; n < D_out; ++n) z[n]"),
+    "pl_bwd_w_not_transposed": ("s += bf16_to_double(dy[n]) * bf16_to_double(wr[n]);",
+                                "s += bf16_to_double(dy[n]) * bf16_to_double(we[(n * D_in + d) % (D_in * D_out)]);"),
+    "pl_bwd_dx_gate_dropped": ("for (int64_t i = 0; i < D_in; ++i) o[i] += g * c[i];",
+                               "for (int64_t i = 0; i < D_in; ++i) o[i] += c[i];"),
+    "pl_bwd_dx_grouped_in_route_order": ("double *o = grouped_in ? dx + r * D_in : dx + t * D_in;",
+                                         "double *o = grouped_in ? dx + f * D_in : dx + t * D_in;"),
+    "pl_bwd_dw_gate_dropped": ("double xa = g * bf16_to_double(in[a]);", "double xa = bf16_to_double(in[a]);"),
+    "pl_bwd_dw_wrong_expert": ("double *we = dw + e * D_in * D_out;", "double *we = dw + ((e + 1) % E) * D_in * D_out;"),
+    "pl_bwd_dg_gated": ("s += bf16_to_double(d[b]) * c[b];", "s += (gates ? gates[f] : 1.0) * bf16_to_double(d[b]) * c[b];"),
+    "pl_bwd_dg_first_term_dropped": ("for (int64_t b = 0; b < D_out; ++b) s += bf16_to_double(d[b]) * c[b];",
+                                     "for (int64_t b = 1; b < D_out; ++b) s += bf16_to_double(d[b]) * c[b];"),
 }
 
 
