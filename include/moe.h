@@ -2,7 +2,8 @@
  * moe.h -- C ABI of the dropless sparse Mixture-of-Experts forward path for
  * AMD Instinct MI355X (gfx950).
  *
- * The forward pass has four stages. This library exports them as three calls:
+ * The forward pass has four stages. This library exports them as three calls
+ * (plus the general ParallelLinear primitive and its backward, below):
  *
  *   moe_route_topk       router: H(X) = Softmax(TopK(X W_gate, k))
  *                        (ScatterMoE Guide, section "1. The Dynamic Routing
@@ -169,6 +170,62 @@ int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
                         const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
                         int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *out,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes of moe_parallel_linear_fwd and moe_parallel_linear_bwd for
+ * these sizes (one size serves every grouping mode and both calls): tile
+ * tables, fp32 rows [S*k, max(D_in, D_out)] and the bf16 slot-order rows the
+ * weight gradient reads. Pure host function.
+ */
+size_t moe_parallel_linear_workspace_bytes(int32_t S, int32_t k, int32_t D_in, int32_t D_out, int32_t E);
+
+/*
+ * ParallelLinear(X, W, I, G) (ScatterMoE Guide, "1. The Anatomy of
+ * ParallelLinear" and the figure "The ParallelLinear Core Abstraction": rows
+ * of X read by index, multiplied by the routed expert's W, scaled by the
+ * router coefficient, with grouped (expert-sorted) or scattered (token
+ * order) layouts on either side). With f = t*k + j the route of token t to
+ * expert e in slot r (the map of moe_sparse_map):
+ *   in(f) = x[r] if grouped_in (x holds S*k rows in slot order),
+ *           x[t] otherwise (x holds S token rows, read in place)
+ *   z_f   = g_f * in(f) W[e]    (fp32 sums; g_f = gates[f], 1 if gates == NULL)
+ *   y[r]  = bf16(z_f)                if grouped_out (y: S*k rows, slot order)
+ *   y[t]  = bf16(sum_j z_f)          otherwise (y: S rows; j = 0..k-1 in order,
+ *                                    rounded once)
+ * w [E, D_in, D_out] bf16 (D_out contiguous); gates [S*k] fp32 or NULL;
+ * expert_offsets [E+1] and slot_src [S*k] from moe_sparse_map; grouped_in
+ * and grouped_out are 0 or 1. The output is fully written.
+ * Limits: D_in % 64 == 0, D_out % 64 == 0, E <= 1024,
+ * S*k*max(D_in, D_out) < 2^30, D_in*D_out < 2^30 (else UNSUPPORTED).
+ */
+int moe_parallel_linear_fwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
+                            const int32_t *slot_src, int32_t S, int32_t k, int32_t D_in, int32_t D_out, int32_t E,
+                            int32_t grouped_in, int32_t grouped_out, uint16_t *y, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of ParallelLinear (ScatterMoE Guide, "3. Fused Backward Pass
+ * Dynamics": the input gradient scatters g dY W_e^T back to the rows it came
+ * from, the weight gradient accumulates g x^T dY over each expert's tokens).
+ * With dy_f = dy[r] if grouped_out, else dy[t] (dy laid out like the
+ * forward's y):
+ *   dx     [like x]           c_f = dy_f W[e]^T (fp32); dx[r] = bf16(g_f c_f)
+ *                             if grouped_in, else dx[t] = bf16(sum_j g_f c_f)
+ *   dw     [E, D_in, D_out]   fp32; dw[e] = sum over the slots of expert e of
+ *                             in(f)^T (g_f dy_f), the reduction kept on chip
+ *                             (one workgroup owns each output tile: no
+ *                             atomics); an expert with no routes gets zeros
+ *   dgates [S*k]              fp32; dgates[f] = <dy_f, in(f) W[e]>, the
+ *                             gradient of the router coefficient
+ * Any of dx, dw, dgates may be NULL (not all three). For dw the product
+ * g_f * dy_f is rounded to bf16 before the GEMM. Reproducible run to run.
+ * Arguments and limits as moe_parallel_linear_fwd; with S == 0 only dw is
+ * written (zeros).
+ */
+int moe_parallel_linear_bwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
+                            const int32_t *slot_src, const uint16_t *dy, int32_t S, int32_t k, int32_t D_in,
+                            int32_t D_out, int32_t E, int32_t grouped_in, int32_t grouped_out, uint16_t *dx,
+                            float *dw, float *dgates, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Profiling hooks (measurement support, not part of the method). While

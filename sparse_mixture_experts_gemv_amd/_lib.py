@@ -1,6 +1,6 @@
 """ctypes binding of libsmoe.so (C ABI declared in include/moe.h).
 
-Argument marshalling only: every step of the forward pass runs in the HIP
+Argument marshalling only: every step of every call runs in the HIP
 kernels of libsmoe.so. PyTorch supplies device memory and the current HIP
 stream. There is no fallback: if the library is missing or a call fails, an
 exception is raised.
@@ -31,6 +31,11 @@ SIGNATURES = {
     "moe_scatter_ffn_workspace_bytes_atomic": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_scatter_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ,
                                            _P]),
+    "moe_parallel_linear_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "moe_parallel_linear_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
+                                               _SZ, _P]),
+    "moe_parallel_linear_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
+                                               _P, _P, _P, _SZ, _P]),
     "moe_profile_start": (ctypes.c_int, [ctypes.c_int]),
     "moe_profile_stop": (ctypes.c_int, []),
     "moe_profile_kinds": (ctypes.c_int, []),
@@ -193,6 +198,68 @@ def moe_scatter_ffn_fwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2:
                                       _ptr(expert_offsets), _ptr(slot_src), S, D, F, E, k, _ptr(out), _ptr(ws),
                                       need, _stream(stream)), "moe_scatter_ffn_fwd")
     return out
+
+
+def parallel_linear_workspace_bytes(S: int, k: int, D_in: int, D_out: int, E: int) -> int:
+    return int(load().moe_parallel_linear_workspace_bytes(S, k, D_in, D_out, E))
+
+
+def _pl_shapes(x, w, expert_offsets, slot_src, k, grouped_in):
+    E, D_in, D_out = w.shape
+    n_in = x.shape[0]
+    S = n_in // k if grouped_in else n_in
+    if grouped_in and n_in != S * k:
+        raise MoEError("grouped input must hold S*k rows")
+    _dev(x, torch.bfloat16, "x", (n_in, D_in))
+    _dev(w, torch.bfloat16, "w")
+    _dev(expert_offsets, torch.int32, "expert_offsets", (E + 1,))
+    _dev(slot_src, torch.int32, "slot_src", (S * k,))
+    return S, E, D_in, D_out
+
+
+def moe_parallel_linear_fwd(x: torch.Tensor, w: torch.Tensor, gates: Optional[torch.Tensor],
+                            expert_offsets: torch.Tensor, slot_src: torch.Tensor, k: int, grouped_in: bool = False,
+                            grouped_out: bool = False, y: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ParallelLinear(X, W, I, G) -> y bf16 [S*k (grouped_out) or S, D_out]; gates fp32 [S, k] or None."""
+    S, E, D_in, D_out = _pl_shapes(x, w, expert_offsets, slot_src, k, grouped_in)
+    if gates is not None:
+        _dev(gates, torch.float32, "gates", (S, k))
+    rows = S * k if grouped_out else S
+    if y is None:
+        y = torch.empty((rows, D_out), dtype=torch.bfloat16, device=x.device)
+    _dev(y, torch.bfloat16, "y", (rows, D_out))
+    need = parallel_linear_workspace_bytes(S, k, D_in, D_out, E)
+    ws = _workspace(need, x.device, workspace)
+    _check(load().moe_parallel_linear_fwd(_ptr(x), _ptr(w), _ptr(gates), _ptr(expert_offsets), _ptr(slot_src), S, k,
+                                          D_in, D_out, E, int(grouped_in), int(grouped_out), _ptr(y), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_parallel_linear_fwd")
+    return y
+
+
+def moe_parallel_linear_bwd(x: torch.Tensor, w: torch.Tensor, gates: Optional[torch.Tensor],
+                            expert_offsets: torch.Tensor, slot_src: torch.Tensor, dy: torch.Tensor, k: int,
+                            grouped_in: bool = False, grouped_out: bool = False, need_dx: bool = True,
+                            need_dw: bool = True, need_dgates: bool = True, workspace: Optional[torch.Tensor] = None,
+                            stream=None):
+    """Backward of ParallelLinear -> (dx bf16 like x, dw fp32 [E, D_in, D_out], dgates fp32 [S, k]);
+    an output not requested is None."""
+    S, E, D_in, D_out = _pl_shapes(x, w, expert_offsets, slot_src, k, grouped_in)
+    if gates is not None:
+        _dev(gates, torch.float32, "gates", (S, k))
+    _dev(dy, torch.bfloat16, "dy", ((S * k if grouped_out else S), D_out))
+    dev = x.device
+    dx = torch.empty_like(x) if need_dx else None
+    dw = torch.empty((E, D_in, D_out), dtype=torch.float32, device=dev) if need_dw else None
+    dg = torch.empty((S, k), dtype=torch.float32, device=dev) if need_dgates else None
+    need = parallel_linear_workspace_bytes(S, k, D_in, D_out, E)
+    ws = _workspace(need, dev, workspace)
+    _check(load().moe_parallel_linear_bwd(_ptr(x), _ptr(w), _ptr(gates), _ptr(expert_offsets), _ptr(slot_src),
+                                          _ptr(dy), S, k, D_in, D_out, E, int(grouped_in), int(grouped_out),
+                                          _ptr(dx), _ptr(dw), _ptr(dg), _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream)), "moe_parallel_linear_bwd")
+    return dx, dw, dg
 
 
 class MoELayer:

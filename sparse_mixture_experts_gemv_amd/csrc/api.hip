@@ -110,4 +110,68 @@ int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
                                            workspace, use_atomic, reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t moe_parallel_linear_workspace_bytes(int32_t S, int32_t k, int32_t D_in, int32_t D_out, int32_t E) {
+    if (S < 0 || k < 1 || D_in < 1 || D_out < 1 || E < 1) return 0;
+    return smoe::pl_plan(S, k, D_in, D_out, E).ws_bytes;
+}
+
+namespace {
+
+// Shared checks of the ParallelLinear calls; returns MOE_OK or an error.
+int pl_check(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
+             const int32_t *slot_src, int32_t S, int32_t k, int32_t D_in, int32_t D_out, int32_t E,
+             int32_t grouped_in, int32_t grouped_out, void *workspace, size_t workspace_bytes) {
+    if (S < 0 || k < 1 || E < 1 || k > E || D_in < 1 || D_out < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if ((grouped_in != 0 && grouped_in != 1) || (grouped_out != 0 && grouped_out != 1))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!w || !expert_offsets || !workspace || (S > 0 && (!x || !slot_src))) return MOE_ERR_INVALID_ARGUMENT;
+    if ((x && misaligned(x)) || misaligned(w) || misaligned(expert_offsets) || (slot_src && misaligned(slot_src)) ||
+        misaligned(workspace) || (gates && misaligned(gates)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (D_in % 64 != 0 || D_out % 64 != 0 || E > 1024) return MOE_ERR_UNSUPPORTED;
+    const int64_t N = (int64_t)S * k;
+    // 32-bit buffer offsets: every row buffer and each expert matrix stay below 2 GiB
+    if (N * (int64_t)(D_in > D_out ? D_in : D_out) >= ((int64_t)1 << 30) ||
+        (int64_t)D_in * D_out >= ((int64_t)1 << 30))
+        return MOE_ERR_UNSUPPORTED;
+    const smoe::PlPlan pl = smoe::pl_plan(S, k, D_in, D_out, E);
+    if (!smoe::pl_plan_fits(pl)) return MOE_ERR_UNSUPPORTED;
+    if (workspace_bytes < pl.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return MOE_OK;
+}
+
+}  // namespace
+
+int moe_parallel_linear_fwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
+                            const int32_t *slot_src, int32_t S, int32_t k, int32_t D_in, int32_t D_out, int32_t E,
+                            int32_t grouped_in, int32_t grouped_out, uint16_t *y, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    if (S < 0 || k < 1 || E < 1 || k > E || D_in < 1 || D_out < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (S == 0) return MOE_OK;
+    if (!y || misaligned(y)) return MOE_ERR_INVALID_ARGUMENT;
+    const int st = pl_check(x, w, gates, expert_offsets, slot_src, S, k, D_in, D_out, E, grouped_in, grouped_out,
+                            workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    return finish(smoe::launch_pl_fwd(x, w, gates, expert_offsets, slot_src, S, k, D_in, D_out, E, grouped_in != 0,
+                                      grouped_out != 0, y, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_parallel_linear_bwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
+                            const int32_t *slot_src, const uint16_t *dy, int32_t S, int32_t k, int32_t D_in,
+                            int32_t D_out, int32_t E, int32_t grouped_in, int32_t grouped_out, uint16_t *dx,
+                            float *dw, float *dgates, void *workspace, size_t workspace_bytes, void *stream) {
+    if (S < 0 || k < 1 || E < 1 || k > E || D_in < 1 || D_out < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (!dx && !dw && !dgates) return MOE_ERR_INVALID_ARGUMENT;
+    if (S == 0 && !dw) return MOE_OK;  // with dw, the zero gradient is still written
+    if ((S > 0 && !dy) || (dy && misaligned(dy)) || (dx && misaligned(dx)) || (dw && misaligned(dw)) ||
+        (dgates && misaligned(dgates)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    const int st = pl_check(x, w, gates, expert_offsets, slot_src, S, k, D_in, D_out, E, grouped_in, grouped_out,
+                            workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    return finish(smoe::launch_pl_bwd(x, w, gates, expert_offsets, slot_src, dy, S, k, D_in, D_out, E,
+                                      grouped_in != 0, grouped_out != 0, dx, dw, dgates, workspace,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -30,13 +30,6 @@ namespace smoe {
 // thread finds the expert of a block by binary search over T_e. Two GEMMs
 // (tile heights) are handled in one launch. Entries past the real tile count
 // are marked empty (expert = -1, order M field all ones).
-struct TileTableArgs {
-    int bm[2], n_mtiles[2], n_ntiles[2];
-    int4 *tiles[2];
-    uint32_t *order[2];
-    int *valid[2];  // number of non-empty M tiles
-};
-
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restrict__ offsets, int E, int N,
                                                           const TileTableArgs a) {
     __shared__ int s_wave[2][16];
@@ -148,12 +141,26 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float4 *__restr
     }
 }
 
+void launch_tile_table(const int32_t *offsets, int E, int N, const TileTableArgs &a, hipStream_t stream) {
+    prof_begin(stream, kKTileTable);
+    tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, E, N, a);
+    prof_end(stream, kKTileTable);
+}
+
+void launch_combine_rows(const float *y, uint16_t *out, int S, int D, int k, hipStream_t stream) {
+    const size_t n4 = (size_t)S * D / 4;
+    prof_begin(stream, kKCombine);
+    combine_rows_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(y),
+                                                                    reinterpret_cast<uint2 *>(out), S, D / 4, k);
+    prof_end(stream, kKCombine);
+}
+
 // Tile height per GEMM from the mean rows per expert (known on the host
 // without reading the device-side counts): 256 rows from 192 up, 192 rows
 // from 96 (an expert of ~128 +- 3 sigma rows fits one tile, so its weights
 // stream once), 64 rows from 48, else 32 rows (decode-sized batches: the
 // weights dominate and a shallow tile keeps the MFMA work small).
-static int pick_bm(int64_t avg) {
+int pick_bm(int64_t avg) {
     if (avg >= 192) return 256;
     if (avg >= 96) return 192;
     if (avg >= 48) return 64;
@@ -171,7 +178,7 @@ static int pick_bm_down(int64_t avg) {
     return pick_bm(avg);
 }
 
-static int tiles_upper_bound(int64_t N, int64_t E, int bm) {
+int tiles_upper_bound(int64_t N, int64_t E, int bm) {
     return (int)((N + std::min(E, N) * (bm - 1)) / bm);
 }
 
@@ -207,12 +214,12 @@ FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k, bool ato
     return pl;
 }
 
-static int grid_for(size_t n, int per_block) {
+int grid_for(size_t n, int per_block) {
     const size_t b = (n + per_block - 1) / per_block;
     return (int)std::min<size_t>(std::max<size_t>(b, 1), 2048);
 }
 
-static int device_cus() {
+int device_cus() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -309,9 +316,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     int *valid_counts = reinterpret_cast<int *>(ws + pl.counts_off);
     ta.valid[0] = valid_counts;
     ta.valid[1] = valid_counts + 1;
-    prof_begin(stream, kKTileTable);
-    tile_table_kernel<<<1, 1024, 0, stream>>>(expert_offsets, E, N, ta);
-    prof_end(stream, kKTileTable);
+    launch_tile_table(expert_offsets, E, N, ta, stream);
     if (atomic) {
         prof_begin(stream, kKAccZero);
         acc_zero_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<float4 *>(acc), n4);
@@ -357,10 +362,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
         prof_end(stream, kKFinalize);
     } else {
         launch_gemm<kDownRows>(pl.bm_down, (int64_t)N / E, p, stream);
-        prof_begin(stream, kKCombine);
-        combine_rows_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
-                                                                        reinterpret_cast<uint2 *>(out), S, D / 4, k);
-        prof_end(stream, kKCombine);
+        launch_combine_rows(acc, out, S, D, k, stream);
     }
     return hipGetLastError();
 }

@@ -19,8 +19,16 @@
 //             buffer (f = the slot's flat route index, so the k rows of a
 //             token are adjacent); a combine pass sums them per token.
 //   kLogits   one B matrix (W_gate), no experts; fp32 store (router logits).
+//   kLinBf16  one B matrix; the tile scales each row by its route's gate
+//             (1 when gate is NULL) and stores it, bf16, to row r of C in
+//             slot order (ParallelLinear with grouped output).
+// kDownRows also treats a NULL gate as 1.
 //
-// Weights are [E, K, N] with N contiguous.
+// Weights are [E, K, N] with N contiguous; with kFlagBT they are [E, N, K]
+// with K contiguous (a weight [E, D_in, D_out] used transposed: the product
+// with W^T that the input gradient needs). gather_a != 0 makes the kDownRows
+// and kLinBf16 tiles read token rows of A in place (row = slot_src[r] / topk),
+// as kGateUp always does.
 #pragma once
 
 #include "common.hpp"
@@ -28,14 +36,15 @@
 
 namespace smoe {
 
-enum GemmMode { kGateUp = 0, kDown = 1, kLogits = 2, kDownRows = 3 };
+enum GemmMode { kGateUp = 0, kDown = 1, kLogits = 2, kDownRows = 3, kLinBf16 = 4 };
+enum GemmFlags { kFlagBT = 1 };
 
 struct GemmParams {
     const uint16_t *A;        // X [S, K] (kGateUp, kLogits) or h [S*k, K] (kDown, kDownRows)
     const uint16_t *B0;       // W1 / W2 / W_gate: [E, K, N]
     const uint16_t *B1;       // W3 (kGateUp only)
     const int32_t *slot_src;  // [S*k] slot -> flat route index
-    const float *gate;        // [S*k] router weights (kDown, kDownRows)
+    const float *gate;        // [S*k] router weights (kDown, kDownRows, kLinBf16; may be NULL except kDown)
     const int4 *tiles;        // [n_mtiles] (expert, row_begin, row_end, -) ; expert < 0 = empty
     const uint32_t *order;    // [n_mtiles * n_ntiles] block order: mt | nt << kOrderMtBits, valid blocks first
     const int *valid_mtiles;  // device count of non-empty M tiles
@@ -45,6 +54,7 @@ struct GemmParams {
     int N;                    // output columns
     int K;                    // reduction length (multiple of 64)
     int topk;                 // k (token = flat route index / k)
+    int gather_a;             // kDownRows / kLinBf16: A rows are token rows read by index
     int n_mtiles;             // M tiles (upper bound over all experts)
     int n_ntiles;             // N tiles
 };

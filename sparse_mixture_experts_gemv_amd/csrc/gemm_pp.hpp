@@ -110,9 +110,10 @@ struct PPGeom {
 // STAGES_A < STAGES the weights, which mostly come from HBM, are requested
 // STAGES - 1 steps ahead and the token rows, mostly L2 hits, STAGES_A - 1
 // steps ahead, within the same LDS budget.
-template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool PARTIAL = false>
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool PARTIAL = false, int FLAGS = 0>
 __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt, int nt, int k_begin, int k_end) {
     constexpr int NB = (MODE == kGateUp) ? 2 : 1;
+    constexpr bool BT = (FLAGS & kFlagBT) != 0;  // B stored [N, K]
     static_assert(BK == 32 || BK == 64, "K step");
     constexpr int KK = BK / 32;                     // MFMA K sub-steps per step
     constexpr int CH = BK / 8;                      // 16-byte chunks per A row
@@ -186,9 +187,10 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
     const uint32_t ldb = (uint32_t)N * 2u;
 
     // ---- DMA sources (group 0 only) ----
-    const uint16_t *a_base = (MODE == kGateUp) ? p.A : p.A + (size_t)row0 * K;
-    const uint32_t a_bytes = (MODE == kGateUp) ? (uint32_t)((size_t)p.A_rows * K * 2)
-                                               : (uint32_t)((size_t)(row1 - row0) * K * 2);
+    // token rows of A read by index (kGateUp always; kDownRows / kLinBf16 on request)
+    const bool gather = (MODE == kGateUp) || ((MODE == kDownRows || MODE == kLinBf16) && p.gather_a);
+    const uint16_t *a_base = gather ? p.A : p.A + (size_t)row0 * K;
+    const uint32_t a_bytes = gather ? (uint32_t)((size_t)p.A_rows * K * 2) : (uint32_t)((size_t)(row1 - row0) * K * 2);
     const pp_i32x4 a_rsrc = pp_desc(a_base, a_bytes);
     const size_t b_off = (size_t)expert * (size_t)K * (size_t)N;
     const uint32_t b_bytes = (uint32_t)((size_t)K * N * 2);
@@ -204,19 +206,26 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
             const int c = (lane % CH) ^ pp_a_swz<CH>(r);
             int slot = row0 + r;
             if (slot >= row1) slot = row1 - 1;      // never stored; keeps gathered reads in range
-            const uint32_t arow =
-                (MODE == kGateUp) ? (uint32_t)(p.slot_src[slot] / p.topk) : (uint32_t)(slot - row0);
+            const uint32_t arow = gather ? (uint32_t)(p.slot_src[slot] / p.topk) : (uint32_t)(slot - row0);
             a_voff[i] = arow * (uint32_t)K * 2u + (uint32_t)c * 16u;
         }
 #pragma unroll
         for (int i = 0; i < B_PER_WAVE; ++i) {
             const int j = wl + 4 * i;
             const int jj = j % B_INSTR_PER_MAT;
-            const int k = jj * B_ROWS_PER_INSTR + lane / B_LANES_PER_ROW;
-            const int pos = lane % B_LANES_PER_ROW;
-            const int seg = (pos >> 1) ^ pp_b_swz<SEGS>(k);
-            const int col = min(n0 + seg * 16 + (pos & 1) * 8, N - 8);  // columns past N feed unstored outputs
-            b_voff[i] = (uint32_t)k * ldb + (uint32_t)col * 2u;
+            if constexpr (BT) {
+                // B^T image like the A image: BN rows (weight rows n), BK K-contiguous
+                const int r = A_ROWS_PER_INSTR * jj + lane / CH;
+                const int c = (lane % CH) ^ pp_a_swz<CH>(r);
+                const int n = min(n0 + r, N - 1);  // rows past N feed unstored outputs
+                b_voff[i] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)c * 16u;
+            } else {
+                const int k = jj * B_ROWS_PER_INSTR + lane / B_LANES_PER_ROW;
+                const int pos = lane % B_LANES_PER_ROW;
+                const int seg = (pos >> 1) ^ pp_b_swz<SEGS>(k);
+                const int col = min(n0 + seg * 16 + (pos & 1) * 8, N - 8);  // columns past N feed unstored outputs
+                b_voff[i] = (uint32_t)k * ldb + (uint32_t)col * 2u;
+            }
         }
     }
 
@@ -230,7 +239,7 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
 #define SMOE_PP_ISSUE_B(KT)                                                                        \
     {                                                                                              \
         const uint32_t sbase = smem_addr + B_RING + SMOE_SLOT_B(KT) * (NB * B_BYTES);              \
-        const uint32_t b_soff = (uint32_t)(KT) * BK * ldb;                                         \
+        const uint32_t b_soff = (uint32_t)(KT) * (BT ? BK * 2u : BK * ldb);                        \
         _Pragma("unroll") for (int i = 0; i < B_PER_WAVE; ++i) {                                   \
             const int j = wl + 4 * i;                                                              \
             pp_dma16((j / B_INSTR_PER_MAT) == 1 ? b_rsrc1 : b_rsrc0, sbase + j * 1024, b_voff[i],  \
@@ -255,9 +264,14 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
         for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int k = kk * 32 + 8 * fg + 4 * h + (fr >> 2);
-                const int n = wn * WTN + j * 16 + 4 * (fr & 3);
-                b_rd[kk][j][h] = k * B_ROW + (((n >> 4) ^ pp_b_swz<SEGS>(k)) << 5) + (n & 15) * 2;
+                if constexpr (BT) {  // one ds_read_b128 per operand, as for A
+                    const int row = wn * WTN + j * 16 + fr;
+                    b_rd[kk][j][h] = row * A_ROW + (((kk * 4 + fg) ^ pp_a_swz<CH>(row)) << 4);
+                } else {
+                    const int k = kk * 32 + 8 * fg + 4 * h + (fr >> 2);
+                    const int n = wn * WTN + j * 16 + 4 * (fr & 3);
+                    b_rd[kk][j][h] = k * B_ROW + (((n >> 4) ^ pp_b_swz<SEGS>(k)) << 5) + (n & 15) * 2;
+                }
             }
 
     f32x4 acc[NB][MT][NT];
@@ -304,9 +318,13 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
-                    const uint2 lo = pp_tr(sb + b * B_BYTES + b_rd[kk][j][0]);
-                    const uint2 hi = pp_tr(sb + b * B_BYTES + b_rd[kk][j][1]);
-                    bf[kk][b][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    if constexpr (BT) {
+                        bf[kk][b][j] = *reinterpret_cast<const uint4 *>(sb + b * B_BYTES + b_rd[kk][j][0]);
+                    } else {
+                        const uint2 lo = pp_tr(sb + b * B_BYTES + b_rd[kk][j][0]);
+                        const uint2 hi = pp_tr(sb + b * B_BYTES + b_rd[kk][j][1]);
+                        bf[kk][b][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    }
                 }
         }
         // reads complete before the barrier: after it the slots may be refilled
@@ -386,12 +404,20 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
                 }
             } else if constexpr (MODE == kDownRows) {
                 const int f = p.slot_src[slot];
-                const float w = p.gate[f];
+                const float w = p.gate ? p.gate[f] : 1.0f;
                 float *yp = reinterpret_cast<float *>(p.C) + (size_t)f * N + n0;
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     const int col = wn * WTN + j * 16 + col_in_tile;
                     if (n0 + col < N) yp[col] = w * acc[0][i][j][r];
+                }
+            } else if constexpr (MODE == kLinBf16) {
+                const float w = p.gate ? p.gate[p.slot_src[slot]] : 1.0f;
+                uint16_t *yp = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) yp[col] = f32_to_bf16_bits(w * acc[0][i][j][r]);
                 }
             } else {
                 float *out = reinterpret_cast<float *>(p.C) + (size_t)slot * N + n0;
@@ -422,7 +448,7 @@ __device__ __forceinline__ bool pp_full_tile(const GemmParams &p, int mt) {
 // (a second copy of the main loop). Measured, that pays where most tiles are
 // short (a 192-row tile over experts of ~100-160 rows: -5 to -7 %), and costs
 // ~3 % where nearly all tiles are full, so only those launches enable it.
-template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool SKIP_ROWS = false>
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool SKIP_ROWS = false, int FLAGS = 0>
 __global__ __launch_bounds__(512) void grouped_gemm_pp_persistent_kernel(const GemmParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[PPGeom<BM, BN, MODE, BK, STAGES, STAGES_A>::SMEM];
     const int total = (*p.valid_mtiles) * p.n_ntiles;
@@ -432,9 +458,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_pp_persistent_kernel(const G
         const int mt = (int)(v & kOrderMtMask), nt = (int)(v >> kOrderMtBits);
         if (mt >= p.n_mtiles) continue;
         if (!SKIP_ROWS || pp_full_tile<BM, MODE>(p, mt))
-            pp_tile<BM, BN, MODE, BK, STAGES, STAGES_A, false>(p, smem, mt, nt, 0, p.K / BK);
+            pp_tile<BM, BN, MODE, BK, STAGES, STAGES_A, false, FLAGS>(p, smem, mt, nt, 0, p.K / BK);
         else
-            pp_tile<BM, BN, MODE, BK, STAGES, STAGES_A, true>(p, smem, mt, nt, 0, p.K / BK);
+            pp_tile<BM, BN, MODE, BK, STAGES, STAGES_A, true, FLAGS>(p, smem, mt, nt, 0, p.K / BK);
     }
 }
 

@@ -44,10 +44,47 @@ inline bool ffn_plan_fits(const FfnPlan &pl) {
     return pl.n_mtiles_up < (int)kOrderMtMask && pl.n_mtiles_down < (int)kOrderMtMask &&
            pl.n_ntiles_up <= kOrderMaxNtiles && pl.n_ntiles_down <= kOrderMaxNtiles;
 }
+// Tile tables of up to two grouped GEMMs (tile heights bm[q]) from the
+// expert offsets: per M tile (expert, row_begin, row_end), an expert-major
+// block order, and the number of non-empty M tiles. A class with
+// n_mtiles = 0 is skipped (its valid counter is still written).
+struct TileTableArgs {
+    int bm[2], n_mtiles[2], n_ntiles[2];
+    int4 *tiles[2];
+    uint32_t *order[2];
+    int *valid[2];  // number of non-empty M tiles
+};
+void launch_tile_table(const int32_t *offsets, int E, int N, const TileTableArgs &a, hipStream_t stream);
+// out[t] = bf16(sum_j y[t k + j]) (fp32 rows [S*k, D] -> bf16 [S, D]), j in order
+void launch_combine_rows(const float *y, uint16_t *out, int S, int D, int k, hipStream_t stream);
+int pick_bm(int64_t avg);
+int tiles_upper_bound(int64_t N, int64_t E, int bm);
+int grid_for(size_t n, int per_block);
+int device_cus();
+
 hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                               const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
                               int S, int D, int F, int E, int k, uint16_t *out, void *workspace, bool atomic,
                               hipStream_t stream);
+
+// ---- ParallelLinear ----
+struct PlPlan {
+    int bm, bn;                  // M tile rows, N tile columns (shared by the forward and input-gradient GEMMs)
+    int n_mtiles, n_ntiles_fwd, n_ntiles_dx;
+    int wg_bm, wg_bn, wg_mt, wg_nt;  // weight-gradient tiles over [D_in, D_out]
+    size_t tiles_off, order_off, counts_off, rows_off, xg_off, dyg_off, ws_bytes;
+};
+PlPlan pl_plan(int64_t S, int64_t k, int64_t D_in, int64_t D_out, int64_t E);
+inline bool pl_plan_fits(const PlPlan &pl) {
+    return pl.n_mtiles < (int)kOrderMtMask && pl.n_ntiles_fwd <= kOrderMaxNtiles && pl.n_ntiles_dx <= kOrderMaxNtiles;
+}
+hipError_t launch_pl_fwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
+                         const int32_t *slot_src, int S, int k, int D_in, int D_out, int E, bool grouped_in,
+                         bool grouped_out, uint16_t *y, void *workspace, hipStream_t stream);
+hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
+                         const int32_t *slot_src, const uint16_t *dy, int S, int k, int D_in, int D_out, int E,
+                         bool grouped_in, bool grouped_out, uint16_t *dx, float *dw, float *dgates,
+                         void *workspace, hipStream_t stream);
 
 // ---- router ----
 size_t route_ws_bytes(int64_t S, int64_t E);

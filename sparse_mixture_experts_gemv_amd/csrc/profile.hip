@@ -37,7 +37,8 @@ Profiler &prof() {
 const char *kNames[kNumKernelIds] = {"route_logits_gemm", "route_topk_softmax", "smap_hist",  "smap_rowscan",
                                      "smap_assign",       "smap_empty",         "ffn_tile_table", "ffn_acc_zero",
                                      "ffn_gate_up_gemm",  "ffn_down_scatter_gemm", "ffn_finalize",
-                                     "ffn_combine"};
+                                     "ffn_combine",       "pl_gemm",            "pl_dx_gemm", "pl_wgrad_gemm",
+                                     "pl_prep",           "pl_finalize"};
 
 }  // namespace
 

@@ -20,6 +20,11 @@ enum KernelId {
     kKDown,
     kKFinalize,
     kKCombine,
+    kKPlGemm,
+    kKPlDxGemm,
+    kKPlWgrad,
+    kKPlPrep,
+    kKPlFinalize,
     kNumKernelIds
 };
 

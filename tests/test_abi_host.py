@@ -28,7 +28,7 @@ def header_functions():
 def test_exports_every_declared_symbol(lib):
     import sparse_mixture_experts_gemv_amd._lib as b
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.SIGNATURES)
@@ -89,6 +89,33 @@ def test_ffn_validation(lib):
     assert f(*args(ws=1024)) == 3
     assert f(*args(S=1, D=1 << 20, F=64)) == 2  # 8192 column tiles of the down GEMM exceed the order table
     assert f(None, None, None, None, None, None, None, 0, 64, 128, 8, 2, None, None, 0, None) == 0
+
+
+def test_parallel_linear_validation(lib):
+    fwd, bwd = lib.moe_parallel_linear_fwd, lib.moe_parallel_linear_bwd
+    fa = lambda S=16, k=2, Di=64, Do=128, E=8, gi=0, go=0, ws=1 << 30, x=FAKE, y=FAKE: (
+        x, FAKE, None, FAKE, FAKE, S, k, Di, Do, E, gi, go, y, FAKE, ws, None)
+    assert fwd(*fa(k=9)) == 1                 # k > E
+    assert fwd(*fa(gi=2)) == 1                # grouping flag not 0/1
+    assert fwd(*fa(x=None)) == 1
+    assert fwd(*fa(y=MISALIGNED)) == 1
+    assert fwd(*fa(Di=96)) == 2               # D_in % 64
+    assert fwd(*fa(Do=80)) == 2               # D_out % 64
+    assert fwd(*fa(E=2048)) == 2
+    assert fwd(*fa(ws=1024)) == 3
+    assert fwd(*fa(S=1 << 20, Di=1024)) == 2  # S*k*D >= 2^30
+    assert fwd(*fa(S=0, x=None, y=None)) == 0
+    ba = lambda dx=FAKE, dw=FAKE, dg=FAKE, S=16, ws=1 << 30, dy=FAKE: (
+        FAKE, FAKE, None, FAKE, FAKE, dy, S, 2, 64, 128, 8, 0, 0, dx, dw, dg, FAKE, ws, None)
+    assert bwd(*ba(dx=None, dw=None, dg=None)) == 1  # nothing requested
+    assert bwd(*ba(dy=None)) == 1
+    assert bwd(*ba(dw=MISALIGNED)) == 1
+    assert bwd(*ba(ws=4096)) == 3
+    assert bwd(*ba(S=0, dw=None)) == 0              # nothing to write
+    n = lib.moe_parallel_linear_workspace_bytes(4096, 2, 4096, 14336, 8)
+    # fp32 rows [S*k, max(D_in, D_out)] + bf16 slot-order copies of x and g*dy + small tables
+    base = 8192 * 14336 * 4 + 8192 * 4096 * 2 + 8192 * 14336 * 2
+    assert base <= n <= base + (1 << 20)
 
 
 def test_workspace_has_no_token_replication(lib):
