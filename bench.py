@@ -10,6 +10,12 @@ Prints one JSON line with the whole-job throughput (tokens/s), the
 roofline of the dominant kernel (timed live with HIP events on its own
 stream over the timed region) and the fp64 CPU oracle timed on a bounded
 sample of the same workload on this host.
+
+--op pl_fwd / pl_bwd time the general ParallelLinear primitive instead, on
+the expert up-projection of the chosen configuration (x [S, D] read by
+index, W [E, D, F], router gates, output grouped [S*k, F]): the forward, or
+the backward producing dx, dw and dgates. Their line reports algorithmic
+TFLOP/s and the roofline of their dominant kernel.
 """
 from __future__ import annotations
 
@@ -91,6 +97,118 @@ def cpu_baseline(cfg, p, target_s: float = 15.0):
                       f"{nthreads} threads, {t_used:.1f} s)"}
 
 
+def pl_cpu_baseline(cfg, p, ids, gates, op, target_s: float = 15.0):
+    """The fp64 oracle's ParallelLinear (forward or backward) on a bounded sample of tokens."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as wl
+
+    o = oracle.get()
+    rng = np.random.default_rng(0)
+    order = rng.permutation(cfg.S)
+    # the backward's dw is [E, D, F'] fp64 per call, so it runs on the first F' = 512 output columns
+    Fs = cfg.F if op == "pl_fwd" else min(cfg.F, 512)
+    w = wl.bf16_bits(p["w1"][:, :, :Fs].contiguous().cpu())
+    done, t_used, flops = 0, 0.0, 0.0
+    n = 2
+    while t_used < target_s and done < cfg.S:
+        toks = np.sort(order[done:done + n])
+        x = wl.bf16_bits(p["x"][torch.from_numpy(toks).to(p["x"].device)].cpu())
+        sid = ids[toks]
+        g = gates[toks].astype(np.float64)
+        t0 = time.perf_counter()
+        if op == "pl_fwd":
+            o.parallel_linear(x, w, sid, g, False, True)
+            flops += 2.0 * sid.size * cfg.D * Fs
+        else:
+            dy = wl.bf16_bits(torch.ones(sid.size, Fs, dtype=torch.bfloat16))
+            o.parallel_linear_bwd(x, w, sid, dy, g, False, True)
+            flops += 4.0 * sid.size * cfg.D * Fs  # the dx and dw products, as counted for the GPU
+        t_used += time.perf_counter() - t0
+        done += n
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} random tokens of the {cfg.name} up-projection ({op}, D_out {Fs}, fp64, 1 thread, "
+                      f"{t_used:.1f} s)"}
+
+
+def bench_parallel_linear(args, cfg, p):
+    """ParallelLinear on the up-projection: x [S, D] by index, W1 [E, D, F], gates, grouped output."""
+    import torch
+
+    import sparse_mixture_experts_gemv_amd as smoe
+
+    S, D, F, E, k = cfg.S, cfg.D, cfg.F, cfg.E, cfg.k
+    x, w = p["x"], p["w1"]
+    if "ids" in p:
+        ids, gates = p["ids"], p["weights"]
+    else:
+        ids, gates = smoe.moe_route_topk(x, p["wg"], k)
+    _, offsets, _, src = smoe.moe_sparse_map(ids, E)
+    N = S * k
+    ws = torch.empty(smoe.parallel_linear_workspace_bytes(S, k, D, F, E), dtype=torch.uint8, device="cuda")
+    y = torch.empty((N, F), dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dy = torch.randn((N, F), generator=g, device="cuda").to(torch.bfloat16)
+    if args.op == "pl_fwd":
+        def step():
+            smoe.moe_parallel_linear_fwd(x, w, gates, offsets, src, k, False, True, y, ws)
+        flops = 2.0 * N * D * F
+        dominant, dom_flops = "pl_gemm", 2.0 * N * D * F
+    else:
+        def step():
+            smoe.moe_parallel_linear_bwd(x, w, gates, offsets, src, dy, k, False, True, workspace=ws)
+        flops = 4.0 * N * D * F  # dx and dw products (dgates is a by-product of the dx rows)
+        dominant, dom_flops = None, 2.0 * N * D * F  # the slower of the dx and dw GEMMs
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    smoe.profile_start(args.steps * 16)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    kern = smoe.profile_stop()
+    ms = t0.elapsed_time(t1) / args.steps
+    if dominant is None:
+        dominant = max(("pl_dx_gemm", "pl_wgrad_gemm"), key=lambda n: kern[n][0] / kern[n][1])
+    dom_ms = kern[dominant][0] / kern[dominant][1]
+    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    rec = {
+        "metric": f"ParallelLinear {'forward' if args.op == 'pl_fwd' else 'backward'} TFLOP/s (up-projection)",
+        "value": round(flops / (ms / 1e3) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} ParallelLinear up-projection ({args.op}; scattered in, grouped out, "
+                               f"gated)", "S": S, "D_in": D, "D_out": F, "E": E, "k": k},
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": dom_flops, "avg_launch_us": round(dom_ms * 1e3, 2)},
+        "kernels": {n: {"avg_us": round(1e3 * tot / c, 2), "launches": c} for n, (tot, c) in kern.items()},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = pl_cpu_baseline(cfg, p, ids.cpu().numpy(), gates.cpu().numpy(), args.op,
+                                              args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +218,8 @@ def main():
     ap.add_argument("--S", type=int, default=None, help="token count (default: the configuration's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--op", default="layer", choices=["layer", "pl_fwd", "pl_bwd"],
+                    help="layer: the MoE forward (default); pl_fwd / pl_bwd: ParallelLinear up-projection")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run three device-to-device copies of BYTES (HBM counter calibration)")
     args = ap.parse_args()
@@ -136,6 +256,9 @@ def main():
     S, D, F, E, k = cfg.S, cfg.D, cfg.F, cfg.E, cfg.k
     print(f"bench: {cfg.describe()} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     p = wl.make_problem(cfg, S=S, device="cuda")
+    if args.op != "layer":
+        bench_parallel_linear(args, cfg, p)
+        return
     layer = smoe.MoELayer(p["wg"], p["w1"], p["w3"], p["w2"], k, S)
     topk = (p["ids"], p["weights"]) if "ids" in p else None
     stream = torch.cuda.current_stream()

@@ -131,14 +131,16 @@ class Oracle:
             raise ValueError(f"oracle_parallel_linear status {st}")
         return y
 
-    def parallel_linear_bwd(self, x_bits, w_bits, ids, dy_bits, gates=None, grouped_in=False, grouped_out=False):
-        """Backward of ParallelLinear -> (dx f64, dw f64 [E, D_in, D_out], dg f64 [S, k])."""
+    def parallel_linear_bwd(self, x_bits, w_bits, ids, dy_bits, gates=None, grouped_in=False, grouped_out=False,
+                            want=("dx", "dw", "dg")):
+        """Backward of ParallelLinear -> (dx f64, dw f64 [E, D_in, D_out], dg f64 [S, k]); outputs not
+        named in `want` are not computed and come back as None."""
         x_bits, w_bits, ids, gates, S, k, E, D_in, D_out = self._pl_args(x_bits, w_bits, ids, gates, grouped_in)
         dy_bits = np.ascontiguousarray(dy_bits, dtype=np.uint16)
         assert dy_bits.shape == ((S * k if grouped_out else S), D_out)
-        dx = np.zeros(((S * k if grouped_in else S), D_in), dtype=np.float64)
-        dw = np.zeros((E, D_in, D_out), dtype=np.float64)
-        dg = np.zeros((S, k), dtype=np.float64)
+        dx = np.zeros(((S * k if grouped_in else S), D_in), dtype=np.float64) if "dx" in want else None
+        dw = np.zeros((E, D_in, D_out), dtype=np.float64) if "dw" in want else None
+        dg = np.zeros((S, k), dtype=np.float64) if "dg" in want else None
         st = self.lib.oracle_parallel_linear_bwd(self._ptr(x_bits), self._ptr(w_bits), self._ptr(gates),
                                                  self._ptr(ids), self._ptr(dy_bits), S, k, D_in, D_out, E,
                                                  int(grouped_in), int(grouped_out), self._ptr(dx), self._ptr(dw),

@@ -127,3 +127,54 @@ def test_parallel_linear_bwd_no_tokens_zeroes_dw():
     _, dw, _ = smoe.moe_parallel_linear_bwd(x, w, None, offsets, src, dy, k, need_dx=False, need_dgates=False)
     torch.cuda.synchronize()
     assert dw.shape == (E, D_in, D_out) and torch.count_nonzero(dw).item() == 0
+
+
+@pytest.mark.parametrize("name,ntok", [("mixtral", 16), ("dsv3", 6)])
+def test_parallel_linear_full_size_sampled(oracle_lib, name, ntok):
+    """The benchmark's configuration (up-projection x [S, D] by index -> grouped [S*k, F], router
+    gates) at full size, checked against the oracle on samples it can compute: forward rows,
+    input-gradient rows and router-gate gradients of sampled tokens (the oracle run on those tokens
+    alone, with only the experts they use), and 64 x 64 blocks of every expert's weight gradient
+    (the oracle on the matching column slices of x and dy, over all tokens)."""
+    import sparse_mixture_experts_gemv_amd as smoe
+    cfg = wl.CONFIGS[name]
+    S, D, F, E, k = cfg.S, cfg.D, cfg.F, cfg.E, cfg.k
+    p = wl.make_problem(cfg, device=DEV)
+    x, w = p["x"], p["w1"]
+    ids, gates = smoe.moe_route_topk(x, p["wg"], k)
+    _, offsets, rows, src = smoe.moe_sparse_map(ids, E)
+    g = torch.Generator(device=DEV).manual_seed(11)
+    dy = torch.randn((S * k, F), generator=g, device=DEV).to(torch.bfloat16)
+    y = smoe.moe_parallel_linear_fwd(x, w, gates, offsets, src, k, False, True)
+    dx, dw, dg = smoe.moe_parallel_linear_bwd(x, w, gates, offsets, src, dy, k, False, True)
+    torch.cuda.synchronize()
+    ids_h, gates_h, rows_h = ids.cpu().numpy(), gates.cpu().numpy().astype(np.float64), rows.cpu().numpy()
+    toks = np.unique(np.concatenate([[0, S - 1], np.random.default_rng(3).choice(S, ntok - 2, replace=False)]))
+    tsel = torch.from_numpy(toks).to(DEV)
+    # sub-problem: the sampled tokens, their experts relabelled 0..U-1 (same order, so the stable
+    # slot order of the sub-problem is the full one restricted to these routes)
+    uniq = np.unique(ids_h[toks])
+    remap = np.full(E, -1, np.int32)
+    remap[uniq] = np.arange(uniq.size, dtype=np.int32)
+    sub_ids, sub_g = remap[ids_h[toks]], gates_h[toks]
+    w_sub = bits(w.index_select(0, torch.from_numpy(uniq.astype(np.int64)).to(DEV)))
+    full_slots = rows_h.reshape(S, k)[toks].reshape(-1)            # route order of the sampled tokens
+    sub_rows = oracle_lib.sparse_map(sub_ids, uniq.size)[2]         # their slots in the sub-problem
+    y_ref = oracle_lib.parallel_linear(bits(x[tsel]), w_sub, sub_ids, sub_g, False, True)
+    assert_close(y[torch.from_numpy(full_slots).to(DEV)].float().cpu().numpy(), y_ref[sub_rows],
+                 f"{name} y (sampled routes)", configured=False)
+    dy_sub = np.zeros((sub_ids.size, F), dtype=np.uint16)
+    dy_sub[sub_rows] = bits(dy[torch.from_numpy(full_slots).to(DEV)])
+    rdx, _, rdg = oracle_lib.parallel_linear_bwd(bits(x[tsel]), w_sub, sub_ids, dy_sub, sub_g, False, True,
+                                                 want=("dx", "dg"))
+    assert_close(dx[tsel].float().cpu().numpy(), rdx, f"{name} dx (sampled tokens)", configured=False)
+    got_dg = dg.cpu().numpy()[toks].astype(np.float64)
+    rel = float(np.max(np.abs(got_dg - rdg)) / np.max(np.abs(rdg)))
+    say(f"  {name} dgates (sampled tokens): max-rel {rel:.3e}")
+    assert rel < 2e-3, rel
+    for (r0, c0) in [(0, 0), (D - 64, F - 64), (D // 2, F // 3 // 64 * 64)]:
+        _, rdw, _ = oracle_lib.parallel_linear_bwd(bits(x[:, r0:r0 + 64]), bits(w[:, r0:r0 + 64, c0:c0 + 64]),
+                                                   ids_h, bits(dy[:, c0:c0 + 64]), gates_h, False, True,
+                                                   want=("dw",))
+        got = dw[:, r0:r0 + 64, c0:c0 + 64].cpu().numpy().astype(np.float64)
+        assert_close(got.reshape(-1, 64), rdw.reshape(-1, 64), f"{name} dw block ({r0}, {c0})", configured=False)
