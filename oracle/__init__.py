@@ -50,6 +50,8 @@ class Oracle:
         L.oracle_parallel_linear_bwd.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_int,
                                                  ctypes.c_int, _P, _P, _P]
         L.oracle_parallel_linear_bwd.restype = ctypes.c_int
+        L.oracle_ffn_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]
+        L.oracle_ffn_bwd.restype = ctypes.c_int
 
     @staticmethod
     def _ptr(a: Optional[np.ndarray]):
@@ -148,6 +150,30 @@ class Oracle:
         if st:
             raise ValueError(f"oracle_parallel_linear_bwd status {st}")
         return dx, dw, dg
+
+    def ffn_bwd(self, x_bits, w1_bits, w3_bits, w2_bits, ids, weights, dout_bits,
+                want=("dx", "dw1", "dw3", "dw2", "dg")):
+        """Backward of the SwiGLU expert FFN with weighted combine -> dict of f64 arrays
+        dx [S, D], dw1 / dw3 [E, D, F], dw2 [E, F, D], dg [S, k] (only those in `want`)."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        S, D = x_bits.shape
+        E, D2, F = w1_bits.shape
+        assert D2 == D and w3_bits.shape == (E, D, F) and w2_bits.shape == (E, F, D)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        k = ids.shape[1]
+        weights = np.ascontiguousarray(weights, dtype=np.float64)
+        dout_bits = np.ascontiguousarray(dout_bits, dtype=np.uint16)
+        assert ids.shape == (S, k) and weights.shape == (S, k) and dout_bits.shape == (S, D)
+        shapes = dict(dx=(S, D), dw1=(E, D, F), dw3=(E, D, F), dw2=(E, F, D), dg=(S, k))
+        out = {n: np.zeros(shapes[n], dtype=np.float64) for n in want}
+        st = self.lib.oracle_ffn_bwd(self._ptr(x_bits), self._ptr(np.ascontiguousarray(w1_bits, dtype=np.uint16)),
+                                     self._ptr(np.ascontiguousarray(w3_bits, dtype=np.uint16)),
+                                     self._ptr(np.ascontiguousarray(w2_bits, dtype=np.uint16)), self._ptr(ids),
+                                     self._ptr(weights), self._ptr(dout_bits), S, D, F, E, k,
+                                     *(self._ptr(out.get(n)) for n in ("dx", "dw1", "dw3", "dw2", "dg")))
+        if st:
+            raise ValueError(f"oracle_ffn_bwd status {st}")
+        return out
 
     def layer(self, x_bits, wg_bits, w1_bits, w3_bits, w2_bits, k, tokens=None, nthreads=None):
         """Route, map and FFN of the whole forward (map returned for inspection)."""

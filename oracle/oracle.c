@@ -388,3 +388,107 @@ int oracle_parallel_linear_bwd(const uint16_t *x, const uint16_t *w, const doubl
     free(rows); free(src); free(c);
     return 0;
 }
+
+/* ------------------------------------------------------------ ffn bwd -- */
+
+/*
+ * Backward of the SwiGLU expert FFN with weighted combine (ScatterMoE Guide,
+ * "3. Fused Backward Pass Dynamics" applied to both linears of the expert
+ * and to the SwiGLU between them). For route f = t*k + j, expert e, gate g:
+ *   a = x W1[e], b = x W3[e], h = SiLU(a) b, y_f = h W2[e]   (forward, fp64)
+ *   dy     = g * dout[t]
+ *   dg[f]  = <dout[t], y_f>
+ *   dh     = dy W2[e]^T
+ *   da     = dh * b * SiLU'(a),  SiLU'(a) = s (1 + a (1 - s)),  s = sigma(a)
+ *   db     = dh * SiLU(a)
+ *   dx[t] += da W1[e]^T + db W3[e]^T          (routes j = 0..k-1 in order)
+ *   dW1[e] += x^T da,  dW3[e] += x^T db,  dW2[e] += h^T dy
+ *                                             (routes in flat order f)
+ * Inputs bf16 bits (dout too); outputs fp64: dx [S, D], dw1 and dw3
+ * [E, D, F], dw2 [E, F, D], dg [S, k]. Any output may be NULL.
+ */
+int oracle_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                   const int32_t *ids, const double *weights, const uint16_t *dout, int64_t S, int64_t D,
+                   int64_t F, int64_t E, int64_t k, double *dx, double *dw1, double *dw3, double *dw2,
+                   double *dg) {
+    if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1) return 1;
+    double *a = (double *)malloc(sizeof(double) * (size_t)F);
+    double *b = (double *)malloc(sizeof(double) * (size_t)F);
+    double *h = (double *)malloc(sizeof(double) * (size_t)F);
+    double *dh = (double *)malloc(sizeof(double) * (size_t)F);
+    double *da = (double *)malloc(sizeof(double) * (size_t)F);
+    double *db = (double *)malloc(sizeof(double) * (size_t)F);
+    double *y = (double *)malloc(sizeof(double) * (size_t)D);
+    double *go = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!a || !b || !h || !dh || !da || !db || !y || !go) {
+        free(a); free(b); free(h); free(dh); free(da); free(db); free(y); free(go);
+        return 2;
+    }
+    if (dx) for (int64_t i = 0; i < S * D; ++i) dx[i] = 0.0;
+    if (dw1) for (int64_t i = 0; i < E * D * F; ++i) dw1[i] = 0.0;
+    if (dw3) for (int64_t i = 0; i < E * D * F; ++i) dw3[i] = 0.0;
+    if (dw2) for (int64_t i = 0; i < E * F * D; ++i) dw2[i] = 0.0;
+    int st = 0;
+    for (int64_t t = 0; t < S; ++t) {
+        const uint16_t *xr = x + t * D;
+        for (int64_t n = 0; n < D; ++n) go[n] = bf16_to_double(dout[t * D + n]);
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t f = t * k + j, e = ids[f];
+            if (e < 0 || e >= E) { st = 1; continue; }
+            const uint16_t *w1e = w1 + e * D * F, *w3e = w3 + e * D * F, *w2e = w2 + e * F * D;
+            double g = weights[f];
+            /* forward of this route */
+            for (int64_t c = 0; c < F; ++c) { a[c] = 0.0; b[c] = 0.0; }
+            for (int64_t d = 0; d < D; ++d) {
+                double xv = bf16_to_double(xr[d]);
+                for (int64_t c = 0; c < F; ++c) {
+                    a[c] += xv * bf16_to_double(w1e[d * F + c]);
+                    b[c] += xv * bf16_to_double(w3e[d * F + c]);
+                }
+            }
+            for (int64_t c = 0; c < F; ++c) h[c] = silu(a[c]) * b[c];
+            if (dg) {
+                for (int64_t n = 0; n < D; ++n) y[n] = 0.0;
+                for (int64_t c = 0; c < F; ++c)
+                    for (int64_t n = 0; n < D; ++n) y[n] += h[c] * bf16_to_double(w2e[c * D + n]);
+                double s = 0.0;
+                for (int64_t n = 0; n < D; ++n) s += go[n] * y[n];
+                dg[f] = s;
+            }
+            /* dh = (g dout) W2^T, then through the SwiGLU */
+            for (int64_t c = 0; c < F; ++c) {
+                double s = 0.0;
+                for (int64_t n = 0; n < D; ++n) s += g * go[n] * bf16_to_double(w2e[c * D + n]);
+                dh[c] = s;
+            }
+            for (int64_t c = 0; c < F; ++c) {
+                double sg = 1.0 / (1.0 + exp(-a[c]));
+                da[c] = dh[c] * b[c] * sg * (1.0 + a[c] * (1.0 - sg));
+                db[c] = dh[c] * silu(a[c]);
+            }
+            if (dx) {
+                for (int64_t d = 0; d < D; ++d) {
+                    double s = 0.0;
+                    for (int64_t c = 0; c < F; ++c)
+                        s += da[c] * bf16_to_double(w1e[d * F + c]) + db[c] * bf16_to_double(w3e[d * F + c]);
+                    dx[t * D + d] += s;
+                }
+            }
+            if (dw1 || dw3) {
+                for (int64_t d = 0; d < D; ++d) {
+                    double xv = bf16_to_double(xr[d]);
+                    for (int64_t c = 0; c < F; ++c) {
+                        if (dw1) dw1[e * D * F + d * F + c] += xv * da[c];
+                        if (dw3) dw3[e * D * F + d * F + c] += xv * db[c];
+                    }
+                }
+            }
+            if (dw2) {
+                for (int64_t c = 0; c < F; ++c)
+                    for (int64_t n = 0; n < D; ++n) dw2[e * F * D + c * D + n] += h[c] * g * go[n];
+            }
+        }
+    }
+    free(a); free(b); free(h); free(dh); free(da); free(db); free(y); free(go);
+    return st;
+}

@@ -327,7 +327,70 @@ def pin_parallel_linear_bwd_dense(o, seed=24):
         assert rel_err(dw1[0], bits_to_f64(q["x"]).T @ bits_to_f64(q["dy"])) < 1e-13, f"E=1 dw {gi}{go}"
 
 
+# ----------------------------------------------------------------- ffn bwd --
+
+def numpy_moe_forward(x, w1, w3, w2, ids, g):
+    """Dense fp64 numpy forward of the routed SwiGLU layer at real-valued inputs:
+    out = sum_e G[:, e] * (SiLU(x W1_e) * (x W3_e)) W2_e with the dense gate matrix G."""
+    S, k = ids.shape
+    E = w1.shape[0]
+    G = np.zeros((S, E))
+    for j in range(k):
+        G[np.arange(S), ids[:, j]] += g[:, j]
+    return sum(G[:, e:e + 1] * dense_swiglu(x, w1[e], w3[e], w2[e]) for e in range(E))
+
+
+def pin_ffn_bwd_finite_differences(o, seed=30):
+    """Every gradient of the backward equals the derivative of the dense numpy forward: along random
+    directions V, <grad, V> = (L(p + eps V) - L(p - eps V)) / (2 eps) with L = <dout, out>, for x, W1,
+    W3, W2 and the gates; includes an expert with no routes (zero weight gradient)."""
+    rng = np.random.default_rng(seed)
+    S, D, F, E, k = 7, 16, 24, 5, 2
+    x = bf16_bits_from_f32(rng.standard_normal((S, D)))
+    w1 = bf16_bits_from_f32(rng.standard_normal((E, D, F)) * D ** -0.5)
+    w3 = bf16_bits_from_f32(rng.standard_normal((E, D, F)) * D ** -0.5)
+    w2 = bf16_bits_from_f32(rng.standard_normal((E, F, D)) * F ** -0.5)
+    ids = np.stack([rng.choice(4, size=2, replace=False) for _ in range(S)]).astype(np.int32)  # expert 4 unused
+    g = rng.dirichlet(np.ones(k), size=S)
+    dout = bf16_bits_from_f32(rng.standard_normal((S, D)))
+    grads = o.ffn_bwd(x, w1, w3, w2, ids, g, dout)
+    P = dict(x=bits_to_f64(x), w1=bits_to_f64(w1), w3=bits_to_f64(w3), w2=bits_to_f64(w2), g=g)
+    G = bits_to_f64(dout)
+    L = lambda q: float(np.sum(G * numpy_moe_forward(q["x"], q["w1"], q["w3"], q["w2"], ids, q["g"])))
+    for name, gname in [("x", "dx"), ("w1", "dw1"), ("w3", "dw3"), ("w2", "dw2"), ("g", "dg")]:
+        for _ in range(2):
+            V = rng.standard_normal(P[name].shape)
+            eps = 1e-5
+            qp = dict(P); qp[name] = P[name] + eps * V
+            qm = dict(P); qm[name] = P[name] - eps * V
+            fd = (L(qp) - L(qm)) / (2 * eps)
+            an = float(np.sum(grads[gname] * V))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), f"{gname}: analytic {an} vs finite difference {fd}"
+    assert np.all(grads["dw1"][4] == 0) and np.all(grads["dw3"][4] == 0) and np.all(grads["dw2"][4] == 0)
+
+
+def pin_ffn_bwd_linear_in_dout(o, seed=31):
+    """The backward is linear in dout: doubling dout (exact in bf16) doubles every gradient exactly;
+    token permutation permutes dx and dg and leaves the weight gradients unchanged up to the order of
+    their sums."""
+    p = small_problem(S=12, D=32, F=40, E=4, k=2, seed=seed)
+    ids, w, _ = o.route(p["x"], p["wg"], 2)
+    rng = np.random.default_rng(seed)
+    d1 = bf16_bits_from_f32(rng.standard_normal((12, 32)))
+    d2 = bf16_bits_from_f32(bits_to_f64(d1).astype(np.float32) * 2.0)
+    a = o.ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], ids, w, d1)
+    b = o.ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], ids, w, d2)
+    for n in a:
+        assert np.array_equal(2.0 * a[n], b[n]), n
+    perm = rng.permutation(12)
+    c = o.ffn_bwd(p["x"][perm], p["w1"], p["w3"], p["w2"], ids[perm], w[perm], d1[perm])
+    assert np.array_equal(c["dx"], a["dx"][perm]) and np.array_equal(c["dg"], a["dg"][perm])
+    for n in ("dw1", "dw3", "dw2"):
+        assert rel_err(c[n], a[n]) < 1e-13, n
+
+
 ALL_PINS = [pin_router_library, pin_router_full_softmax, pin_router_ties, pin_router_given_ids,
             pin_sparse_map, pin_brute_force, pin_dense_single_expert, pin_shared_experts, pin_invariances,
             pin_parallel_linear_dense_mask, pin_parallel_linear_modes, pin_parallel_linear_single_expert,
-            pin_parallel_linear_bwd_adjoint, pin_parallel_linear_bwd_dense]
+            pin_parallel_linear_bwd_adjoint, pin_parallel_linear_bwd_dense, pin_ffn_bwd_finite_differences,
+            pin_ffn_bwd_linear_in_dout]

@@ -49,6 +49,22 @@ MUTANTS = {
     "pl_bwd_dw_gate_dropped": ("double xa = g * bf16_to_double(in[a]);", "double xa = bf16_to_double(in[a]);"),
     "pl_bwd_dw_wrong_expert": ("double *we = dw + e * D_in * D_out;", "double *we = dw + ((e + 1) % E) * D_in * D_out;"),
     "pl_bwd_dg_gated": ("s += bf16_to_double(d[b]) * c[b];", "s += (gates ? gates[f] : 1.0) * bf16_to_double(d[b]) * c[b];"),
+    # expert FFN backward
+    "ffn_bwd_silu_prime_wrong": ("da[c] = dh[c] * b[c] * sg * (1.0 + a[c] * (1.0 - sg));",
+                                 "da[c] = dh[c] * b[c] * sg * (1.0 + a[c] * sg);"),
+    "ffn_bwd_da_db_swapped": ("db[c] = dh[c] * silu(a[c]);", "db[c] = dh[c] * b[c];"),
+    "ffn_bwd_dh_gate_dropped": ("for (int64_t n = 0; n < D; ++n) s += g * go[n] * bf16_to_double(w2e[c * D + n]);",
+                                "for (int64_t n = 0; n < D; ++n) s += go[n] * bf16_to_double(w2e[c * D + n]);"),
+    "ffn_bwd_dx_w3_term_dropped": ("s += da[c] * bf16_to_double(w1e[d * F + c]) + db[c] * bf16_to_double(w3e[d * F + c]);",
+                                   "s += da[c] * bf16_to_double(w1e[d * F + c]);"),
+    "ffn_bwd_dw2_gate_dropped": ("dw2[e * F * D + c * D + n] += h[c] * g * go[n];",
+                                 "dw2[e * F * D + c * D + n] += h[c] * go[n];"),
+    "ffn_bwd_dw1_uses_db": ("if (dw1) dw1[e * D * F + d * F + c] += xv * da[c];",
+                            "if (dw1) dw1[e * D * F + d * F + c] += xv * db[c];"),
+    "ffn_bwd_dg_uses_h": ("for (int64_t n = 0; n < D; ++n) s += go[n] * y[n];",
+                          "for (int64_t n = 0; n < D && n < F; ++n) s += go[n] * h[n];"),
+    "ffn_bwd_w2_not_transposed": ("for (int64_t n = 0; n < D; ++n) s += g * go[n] * bf16_to_double(w2e[c * D + n]);",
+                                  "for (int64_t n = 0; n < D; ++n) s += g * go[n] * bf16_to_double(w2e[(n * F + c) % (F * D)]);"),
     "pl_bwd_dg_first_term_dropped": ("for (int64_t b = 0; b < D_out; ++b) s += bf16_to_double(d[b]) * c[b];",
                                      "for (int64_t b = 1; b < D_out; ++b) s += bf16_to_double(d[b]) * c[b];"),
 }
