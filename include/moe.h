@@ -3,7 +3,8 @@
  * AMD Instinct MI355X (gfx950).
  *
  * The forward pass has four stages. This library exports them as three calls
- * (plus the general ParallelLinear primitive and its backward, below):
+ * (plus, below, the FFN's backward and the general ParallelLinear primitive
+ * with its backward):
  *
  *   moe_route_topk       router: H(X) = Softmax(TopK(X W_gate, k))
  *                        (ScatterMoE Guide, section "1. The Dynamic Routing
@@ -170,6 +171,40 @@ int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
                         const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
                         int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *out,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes of moe_scatter_ffn_bwd: tile tables, the recomputed
+ * a | b [S*k, 2F] and h [S*k, F] (bf16, slot order), slot-order copies of
+ * g*dout and x [S*k, D] (bf16), fp32 input-gradient rows [S*k, D] and the
+ * router-gate partial sums. Pure host function.
+ */
+size_t moe_scatter_ffn_bwd_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k);
+
+/*
+ * Backward of moe_scatter_ffn_fwd (ScatterMoE Guide, "3. Fused Backward Pass
+ * Dynamics": input gradients scattered back through W^T to the token rows,
+ * weight gradients accumulated per expert; "2. The Hidden Cost of Activation
+ * Materialization": the SwiGLU experts). Given dout [S, D] bf16, the
+ * gradient of out, and the forward's inputs, with route f = t*k + j of
+ * expert e in slot r, g = topk_weights[f], a = x[t] W1[e], b = x[t] W3[e],
+ * h = SiLU(a) b (recomputed here, fp32 sums, a and b kept as bf16):
+ *   d_topk_weights[f] = <dout[t], h W2[e]>                          fp32 [S, k]
+ *   c = dout[t] W2[e]^T;  da = g c b SiLU'(a),  db = g c SiLU(a)    (bf16)
+ *   dw2[e] = sum_r h^T (g dout[t])  (g dout[t] rounded to bf16)      fp32 [E, F, D]
+ *   dw1[e] = sum_r x[t]^T da,  dw3[e] = sum_r x[t]^T db             fp32 [E, D, F]
+ *   dx[t]  = bf16(sum_j da W1[e]^T + db W3[e]^T)  (j in order)       bf16 [S, D]
+ * Every weight gradient is reduced on chip per output tile (no atomics);
+ * experts with no routes get zero weight gradients; results are
+ * reproducible run to run. Any output may be NULL (not all). Arguments,
+ * layouts and the map as moe_scatter_ffn_fwd; topk_weights is required.
+ * Limits: D % 64 == 0, F % 64 == 0, E <= 1024, S*D < 2^30, D*F < 2^30,
+ * S*k*max(D, 2F) < 2^30 (else UNSUPPORTED).
+ */
+int moe_scatter_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                        const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                        const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *dx,
+                        float *dw1, float *dw3, float *dw2, float *d_topk_weights, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /*
  * Workspace bytes of moe_parallel_linear_fwd and moe_parallel_linear_bwd for

@@ -31,6 +31,9 @@ SIGNATURES = {
     "moe_scatter_ffn_workspace_bytes_atomic": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_scatter_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ,
                                            _P]),
+    "moe_scatter_ffn_bwd_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "moe_scatter_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                           _P, _P, _P, _SZ, _P]),
     "moe_parallel_linear_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_parallel_linear_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                                _SZ, _P]),
@@ -197,6 +200,39 @@ def moe_scatter_ffn_fwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2:
     _check(load().moe_scatter_ffn_fwd(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(topk_weights),
                                       _ptr(expert_offsets), _ptr(slot_src), S, D, F, E, k, _ptr(out), _ptr(ws),
                                       need, _stream(stream)), "moe_scatter_ffn_fwd")
+    return out
+
+
+def scatter_ffn_bwd_workspace_bytes(S: int, D: int, F: int, E: int, k: int) -> int:
+    return int(load().moe_scatter_ffn_bwd_workspace_bytes(S, D, F, E, k))
+
+
+def moe_scatter_ffn_bwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
+                        topk_weights: torch.Tensor, expert_offsets: torch.Tensor, slot_src: torch.Tensor,
+                        dout: torch.Tensor, need=("dx", "dw1", "dw3", "dw2", "dg"),
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of moe_scatter_ffn_fwd -> dict with dx bf16 [S, D], dw1 / dw3 fp32 [E, D, F],
+    dw2 fp32 [E, F, D] and dg fp32 [S, k] (the router-weight gradient), for the names in `need`."""
+    S, D = x.shape
+    E, D2, F = w1.shape
+    k = topk_weights.shape[1]
+    _dev(x, torch.bfloat16, "x")
+    _dev(w1, torch.bfloat16, "w1", (E, D, F))
+    _dev(w3, torch.bfloat16, "w3", (E, D, F))
+    _dev(w2, torch.bfloat16, "w2", (E, F, D))
+    _dev(topk_weights, torch.float32, "topk_weights", (S, k))
+    _dev(expert_offsets, torch.int32, "expert_offsets", (E + 1,))
+    _dev(slot_src, torch.int32, "slot_src", (S * k,))
+    _dev(dout, torch.bfloat16, "dout", (S, D))
+    dev = x.device
+    shapes = dict(dx=((S, D), torch.bfloat16), dw1=((E, D, F), torch.float32), dw3=((E, D, F), torch.float32),
+                  dw2=((E, F, D), torch.float32), dg=((S, k), torch.float32))
+    out = {n: torch.empty(shapes[n][0], dtype=shapes[n][1], device=dev) for n in need}
+    ws = _workspace(scatter_ffn_bwd_workspace_bytes(S, D, F, E, k), dev, workspace)
+    _check(load().moe_scatter_ffn_bwd(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(topk_weights),
+                                      _ptr(expert_offsets), _ptr(slot_src), _ptr(dout), S, D, F, E, k,
+                                      *(_ptr(out.get(n)) for n in ("dx", "dw1", "dw3", "dw2", "dg")), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)), "moe_scatter_ffn_bwd")
     return out
 
 

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsmoe.so")
-SOURCES = ["api.hip", "sparse_map.hip", "route.hip", "ffn.hip", "pl.hip", "profile.hip"]
+SOURCES = ["api.hip", "sparse_map.hip", "route.hip", "ffn.hip", "ffn_bwd.hip", "pl.hip", "profile.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -110,6 +110,39 @@ int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
                                            workspace, use_atomic, reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t moe_scatter_ffn_bwd_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k) {
+    if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1) return 0;
+    return smoe::ffn_bwd_plan(S, D, F, E, k).ws_bytes;
+}
+
+int moe_scatter_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                        const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                        const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *dx,
+                        float *dw1, float *dw3, float *dw2, float *d_topk_weights, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if (!dx && !dw1 && !dw3 && !dw2 && !d_topk_weights) return MOE_ERR_INVALID_ARGUMENT;
+    if (!w1 || !w3 || !w2 || !expert_offsets || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+    if (S > 0 && (!x || !topk_weights || !slot_src || !dout)) return MOE_ERR_INVALID_ARGUMENT;
+    const void *ptrs[] = {x, w1, w3, w2, topk_weights, expert_offsets, slot_src, dout, dx, dw1, dw3, dw2,
+                          d_topk_weights, workspace};
+    for (const void *q : ptrs)
+        if (q && misaligned(q)) return MOE_ERR_INVALID_ARGUMENT;
+    if (D % 64 != 0 || F % 64 != 0 || E > 1024) return MOE_ERR_UNSUPPORTED;
+    const int64_t N = (int64_t)S * k;
+    // 32-bit buffer offsets: every row buffer and each expert matrix stay below 2 GiB
+    if (N * (int64_t)(D > 2 * F ? D : 2 * F) >= ((int64_t)1 << 30) || (int64_t)S * D >= ((int64_t)1 << 30) ||
+        (int64_t)D * F >= ((int64_t)1 << 30))
+        return MOE_ERR_UNSUPPORTED;
+    const smoe::FfnBwdPlan pl = smoe::ffn_bwd_plan(S, D, F, E, k);
+    if (!smoe::ffn_bwd_plan_fits(pl)) return MOE_ERR_UNSUPPORTED;
+    if (workspace_bytes < pl.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (S == 0 && !dw1 && !dw3 && !dw2) return MOE_OK;  // with a weight gradient requested, zeros are written
+    return finish(smoe::launch_ffn_bwd(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, dout, S, D, F, E, k,
+                                       dx, dw1, dw3, dw2, d_topk_weights, workspace,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t moe_parallel_linear_workspace_bytes(int32_t S, int32_t k, int32_t D_in, int32_t D_out, int32_t E) {
     if (S < 0 || k < 1 || D_in < 1 || D_out < 1 || E < 1) return 0;
     return smoe::pl_plan(S, k, D_in, D_out, E).ws_bytes;

@@ -22,13 +22,25 @@
 //   kLinBf16  one B matrix; the tile scales each row by its route's gate
 //             (1 when gate is NULL) and stores it, bf16, to row r of C in
 //             slot order (ParallelLinear with grouped output).
+//   kGateUpSave  as kGateUp (gathered A, W1 and W3), for the backward's
+//             recomputation: stores a = bf16(A W1) and b = bf16(A W3) side by
+//             side in C ([rows, 2N]: a in columns [0, N), b in [N, 2N)) and
+//             h = bf16(SiLU(a) * b) from the fp32 sums in C2 ([rows, N]).
+//   kSwigluBwd  one B matrix (W2 used transposed: kFlagBT), gathered A (the
+//             output gradient rows of the tokens): c = dout[t] W2[e]^T; with
+//             the route's gate g and the saved a, b of C it writes, in place,
+//             da = g c b SiLU'(a) over a and db = g c SiLU(a) over b, and adds
+//             <h, c> over the tile's columns into part[(nt * 4 + wn) * M + f]
+//             (the router-gate gradient, summed later in a fixed order).
 // kDownRows also treats a NULL gate as 1.
 //
 // Weights are [E, K, N] with N contiguous; with kFlagBT they are [E, N, K]
 // with K contiguous (a weight [E, D_in, D_out] used transposed: the product
 // with W^T that the input gradient needs). gather_a != 0 makes the kDownRows
 // and kLinBf16 tiles read token rows of A in place (row = slot_src[r] / topk),
-// as kGateUp always does.
+// as kGateUp always does. kFlagKSplit (with kFlagBT) splits K in two halves:
+// k < K/2 reads B0 and k >= K/2 reads B1, each [E, N, K/2] (the input
+// gradient of the SwiGLU experts: [da | db] times [W1 ; W3]^T).
 #pragma once
 
 #include "common.hpp"
@@ -36,8 +48,8 @@
 
 namespace smoe {
 
-enum GemmMode { kGateUp = 0, kDown = 1, kLogits = 2, kDownRows = 3, kLinBf16 = 4 };
-enum GemmFlags { kFlagBT = 1 };
+enum GemmMode { kGateUp = 0, kDown = 1, kLogits = 2, kDownRows = 3, kLinBf16 = 4, kGateUpSave = 5, kSwigluBwd = 6 };
+enum GemmFlags { kFlagBT = 1, kFlagKSplit = 2 };
 
 struct GemmParams {
     const uint16_t *A;        // X [S, K] (kGateUp, kLogits) or h [S*k, K] (kDown, kDownRows)
@@ -49,6 +61,9 @@ struct GemmParams {
     const uint32_t *order;    // [n_mtiles * n_ntiles] block order: mt | nt << kOrderMtBits, valid blocks first
     const int *valid_mtiles;  // device count of non-empty M tiles
     void *C;                  // h bf16 [S*k, N] / acc fp32 [S, N] / y fp32 [S*k, N] / logits fp32 [S, N]
+                              // / a|b bf16 [S*k, 2N] (kGateUpSave, kSwigluBwd)
+    void *C2;                 // h bf16 [S*k, N] (kGateUpSave)
+    float *part;              // router-gate partial sums (kSwigluBwd)
     int M;                    // rows (kLogits: S); A has M rows unless gathered
     int A_rows;               // rows of A (gathered: S)
     int N;                    // output columns

@@ -98,7 +98,7 @@ __device__ __forceinline__ int pp_b_swz(int k) {
 // LDS: a ring of STAGES_A k-steps of A and a ring of STAGES k-steps of B.
 template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES>
 struct PPGeom {
-    static constexpr int NB = (MODE == kGateUp) ? 2 : 1;
+    static constexpr int NB = (MODE == kGateUp || MODE == kGateUpSave) ? 2 : 1;
     static constexpr int SMEM = STAGES_A * BM * BK * 2 + STAGES * NB * BK * BN * 2;
 };
 
@@ -112,8 +112,10 @@ struct PPGeom {
 // steps ahead, within the same LDS budget.
 template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool PARTIAL = false, int FLAGS = 0>
 __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt, int nt, int k_begin, int k_end) {
-    constexpr int NB = (MODE == kGateUp) ? 2 : 1;
-    constexpr bool BT = (FLAGS & kFlagBT) != 0;  // B stored [N, K]
+    constexpr int NB = (MODE == kGateUp || MODE == kGateUpSave) ? 2 : 1;
+    constexpr bool BT = (FLAGS & kFlagBT) != 0;          // B stored [N, K]
+    constexpr bool KSPLIT = (FLAGS & kFlagKSplit) != 0;  // k < K/2 from B0, k >= K/2 from B1
+    static_assert(!KSPLIT || (BT && NB == 1), "K split is for one transposed B");
     static_assert(BK == 32 || BK == 64, "K step");
     constexpr int KK = BK / 32;                     // MFMA K sub-steps per step
     constexpr int CH = BK / 8;                      // 16-byte chunks per A row
@@ -188,14 +190,16 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
 
     // ---- DMA sources (group 0 only) ----
     // token rows of A read by index (kGateUp always; kDownRows / kLinBf16 on request)
-    const bool gather = (MODE == kGateUp) || ((MODE == kDownRows || MODE == kLinBf16) && p.gather_a);
+    const bool gather = (MODE == kGateUp || MODE == kGateUpSave) ||
+                        ((MODE == kDownRows || MODE == kLinBf16 || MODE == kSwigluBwd) && p.gather_a);
     const uint16_t *a_base = gather ? p.A : p.A + (size_t)row0 * K;
     const uint32_t a_bytes = gather ? (uint32_t)((size_t)p.A_rows * K * 2) : (uint32_t)((size_t)(row1 - row0) * K * 2);
     const pp_i32x4 a_rsrc = pp_desc(a_base, a_bytes);
-    const size_t b_off = (size_t)expert * (size_t)K * (size_t)N;
-    const uint32_t b_bytes = (uint32_t)((size_t)K * N * 2);
+    const int KB = KSPLIT ? K / 2 : K;  // K extent of one B matrix
+    const size_t b_off = (size_t)expert * (size_t)KB * (size_t)N;
+    const uint32_t b_bytes = (uint32_t)((size_t)KB * N * 2);
     const pp_i32x4 b_rsrc0 = pp_desc(p.B0 + b_off, b_bytes);
-    const pp_i32x4 b_rsrc1 = pp_desc((NB == 2 ? p.B1 : p.B0) + b_off, b_bytes);
+    const pp_i32x4 b_rsrc1 = pp_desc((NB == 2 || KSPLIT ? p.B1 : p.B0) + b_off, b_bytes);
     const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
     uint32_t a_voff[A_PER_WAVE], b_voff[B_PER_WAVE];
     if (group == 0) {
@@ -218,7 +222,7 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
                 const int r = A_ROWS_PER_INSTR * jj + lane / CH;
                 const int c = (lane % CH) ^ pp_a_swz<CH>(r);
                 const int n = min(n0 + r, N - 1);  // rows past N feed unstored outputs
-                b_voff[i] = (uint32_t)n * (uint32_t)K * 2u + (uint32_t)c * 16u;
+                b_voff[i] = (uint32_t)n * (uint32_t)KB * 2u + (uint32_t)c * 16u;
             } else {
                 const int k = jj * B_ROWS_PER_INSTR + lane / B_LANES_PER_ROW;
                 const int pos = lane % B_LANES_PER_ROW;
@@ -239,11 +243,12 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
 #define SMOE_PP_ISSUE_B(KT)                                                                        \
     {                                                                                              \
         const uint32_t sbase = smem_addr + B_RING + SMOE_SLOT_B(KT) * (NB * B_BYTES);              \
-        const uint32_t b_soff = (uint32_t)(KT) * (BT ? BK * 2u : BK * ldb);                        \
+        const bool hi_ = KSPLIT && (KT) * BK >= KB;                                                \
+        const uint32_t b_soff = (uint32_t)((KT) - (hi_ ? KB / BK : 0)) * (BT ? BK * 2u : BK * ldb); \
         _Pragma("unroll") for (int i = 0; i < B_PER_WAVE; ++i) {                                   \
             const int j = wl + 4 * i;                                                              \
-            pp_dma16((j / B_INSTR_PER_MAT) == 1 ? b_rsrc1 : b_rsrc0, sbase + j * 1024, b_voff[i],  \
-                     b_soff);                                                                      \
+            pp_dma16(((j / B_INSTR_PER_MAT) == 1 || hi_) ? b_rsrc1 : b_rsrc0, sbase + j * 1024,    \
+                     b_voff[i], b_soff);                                                           \
         }                                                                                          \
     }
 
@@ -411,6 +416,45 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
                     const int col = wn * WTN + j * 16 + col_in_tile;
                     if (n0 + col < N) yp[col] = w * acc[0][i][j][r];
                 }
+            } else if constexpr (MODE == kGateUpSave) {
+                uint16_t *ab = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * (2 * N) + n0;
+                uint16_t *hh = reinterpret_cast<uint16_t *>(p.C2) + (size_t)slot * N + n0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) {
+                        const float g = acc[0][i][j][r], u = acc[1][i][j][r];
+                        const float sg = g / (1.0f + __expf(-g));  // as the forward kernel
+                        ab[col] = f32_to_bf16_bits(g);
+                        ab[N + col] = f32_to_bf16_bits(u);
+                        hh[col] = f32_to_bf16_bits(sg * u);
+                    }
+                }
+            } else if constexpr (MODE == kSwigluBwd) {
+                const int f = p.slot_src[slot];
+                const float w = p.gate[f];
+                uint16_t *ab = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * (2 * N) + n0;
+                float part = 0.f;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = wn * WTN + j * 16 + col_in_tile;
+                    if (n0 + col < N) {
+                        const float c = acc[0][i][j][r];
+                        const float a = bf16_bits_to_f32(ab[col]), b = bf16_bits_to_f32(ab[N + col]);
+                        const float s = 1.0f / (1.0f + __expf(-a));
+                        const float silu = a * s;
+                        part += silu * b * c;
+                        const float dh = w * c;
+                        ab[col] = f32_to_bf16_bits(dh * b * s * (1.0f + a * (1.0f - s)));
+                        ab[N + col] = f32_to_bf16_bits(dh * silu);
+                    }
+                }
+                // the 16 lanes of this row group hold the row's columns: sum them
+                part += __shfl_xor(part, 8, 16);
+                part += __shfl_xor(part, 4, 16);
+                part += __shfl_xor(part, 2, 16);
+                part += __shfl_xor(part, 1, 16);
+                if (col_in_tile == 0) p.part[(size_t)(nt * WN + wn) * p.M + f] = part;
             } else if constexpr (MODE == kLinBf16) {
                 const float w = p.gate ? p.gate[p.slot_src[slot]] : 1.0f;
                 uint16_t *yp = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * N + n0;

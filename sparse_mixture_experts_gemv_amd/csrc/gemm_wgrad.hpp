@@ -29,10 +29,11 @@ namespace smoe {
 
 struct WgradParams {
     const uint16_t *A;        // [rows, M] slot order
-    const uint16_t *B0, *B1;  // [rows, N] slot order (B1 only when NB = 2)
+    const uint16_t *B0, *B1;  // [rows, N] slot order, row stride ldb (B1 only when NB = 2)
     const int32_t *offsets;   // [E + 1] expert row ranges
     float *C0, *C1;           // [E, M, N]
     int M, N, E;
+    int ldb;                  // row stride of B0 / B1 in elements (>= N)
     int n_mt, n_nt;           // tiles per expert
 };
 
@@ -80,8 +81,9 @@ __device__ __forceinline__ void wg_tile(const WgradParams &p, char *smem, int e,
 
     // descriptors cover exactly this expert's rows: later rows read as zero
     const pp_i32x4 a_rsrc = pp_desc(p.A + (size_t)off * M, (uint32_t)((size_t)rows * M * 2));
-    const pp_i32x4 b_rsrc0 = pp_desc(p.B0 + (size_t)off * N, (uint32_t)((size_t)rows * N * 2));
-    const pp_i32x4 b_rsrc1 = pp_desc((NB == 2 ? p.B1 : p.B0) + (size_t)off * N, (uint32_t)((size_t)rows * N * 2));
+    const int ldb = p.ldb;
+    const pp_i32x4 b_rsrc0 = pp_desc(p.B0 + (size_t)off * ldb, (uint32_t)((size_t)rows * ldb * 2));
+    const pp_i32x4 b_rsrc1 = pp_desc((NB == 2 ? p.B1 : p.B0) + (size_t)off * ldb, (uint32_t)((size_t)rows * ldb * 2));
     const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
     uint32_t a_voff[A_PER_WAVE], b_voff[B_PER_WAVE];
     if (group == 0) {
@@ -102,7 +104,7 @@ __device__ __forceinline__ void wg_tile(const WgradParams &p, char *smem, int e,
             const int pos = lane % B_LANES_PER_ROW;
             const int seg = (pos >> 1) ^ pp_b_swz<BSEGS>(k);
             const int col = min(n0 + seg * 16 + (pos & 1) * 8, N - 8);
-            b_voff[i] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)col * 2u;
+            b_voff[i] = (uint32_t)k * (uint32_t)ldb * 2u + (uint32_t)col * 2u;
         }
     }
     // The whole offset goes in the VGPR operand (scalar offset 0) so that the
@@ -115,7 +117,7 @@ __device__ __forceinline__ void wg_tile(const WgradParams &p, char *smem, int e,
         _Pragma("unroll") for (int i = 0; i < A_PER_WAVE; ++i)                                      \
             pp_dma16(a_rsrc, sa_ + (wl + 4 * i) * 1024, a_voff[i] + astep_, 0u);                    \
         const uint32_t sb_ = smem_addr + B_RING + slot_ * (NB * B_BYTES);                           \
-        const uint32_t bstep_ = (uint32_t)(KT_) * BK * (uint32_t)N * 2u;                            \
+        const uint32_t bstep_ = (uint32_t)(KT_) * BK * (uint32_t)ldb * 2u;                          \
         _Pragma("unroll") for (int i = 0; i < B_PER_WAVE; ++i) {                                    \
             const int j = wl + 4 * i;                                                               \
             pp_dma16((j / B_INSTR_PER_MAT) == 1 ? b_rsrc1 : b_rsrc0, sb_ + j * 1024, b_voff[i] + bstep_, 0u); \

@@ -86,6 +86,24 @@ hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gate
                          bool grouped_in, bool grouped_out, uint16_t *dx, float *dw, float *dgates,
                          void *workspace, hipStream_t stream);
 
+// ---- expert FFN backward ----
+struct FfnBwdPlan {
+    int bm_r, bm_b, bn_b;        // tile rows of the recompute GEMM and of the dh / dx GEMMs; dh / dx tile columns
+    int nm_r, nm_b;              // M tiles (upper bounds)
+    int nn_r, nn_h, nn_x;        // N tiles of the recompute, dh and dx GEMMs
+    int nparts;                  // router-gate partial sums per route
+    size_t tiles_r, tiles_b, order_r, order_h, order_x, counts, ab, h, dyg, xg, rows, part, ws_bytes;
+};
+FfnBwdPlan ffn_bwd_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k);
+inline bool ffn_bwd_plan_fits(const FfnBwdPlan &pl) {
+    return pl.nm_r < (int)kOrderMtMask && pl.nm_b < (int)kOrderMtMask && pl.nn_r <= kOrderMaxNtiles &&
+           pl.nn_h <= kOrderMaxNtiles && pl.nn_x <= kOrderMaxNtiles;
+}
+hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                          const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                          const uint16_t *dout, int S, int D, int F, int E, int k, uint16_t *dx, float *dw1,
+                          float *dw3, float *dw2, float *dg, void *workspace, hipStream_t stream);
+
 // ---- router ----
 size_t route_ws_bytes(int64_t S, int64_t E);
 hipError_t launch_route(const uint16_t *x, const uint16_t *w_gate, int S, int D, int E, int k, int32_t *topk_ids,

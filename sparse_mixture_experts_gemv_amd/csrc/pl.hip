@@ -276,6 +276,7 @@ hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gate
         q.C1 = nullptr;
         q.M = D_in;
         q.N = D_out;
+        q.ldb = D_out;
         q.E = E;
         q.n_mt = pl.wg_mt;
         q.n_nt = pl.wg_nt;

@@ -38,7 +38,8 @@ const char *kNames[kNumKernelIds] = {"route_logits_gemm", "route_topk_softmax", 
                                      "smap_assign",       "smap_empty",         "ffn_tile_table", "ffn_acc_zero",
                                      "ffn_gate_up_gemm",  "ffn_down_scatter_gemm", "ffn_finalize",
                                      "ffn_combine",       "pl_gemm",            "pl_dx_gemm", "pl_wgrad_gemm",
-                                     "pl_prep",           "pl_finalize"};
+                                     "pl_prep",           "pl_finalize",        "bwd_recompute_gemm",
+                                     "bwd_dh_gemm",       "bwd_prep",           "bwd_wgrad_gemm", "bwd_dx_gemm"};
 
 }  // namespace
 

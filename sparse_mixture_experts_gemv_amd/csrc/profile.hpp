@@ -25,6 +25,11 @@ enum KernelId {
     kKPlWgrad,
     kKPlPrep,
     kKPlFinalize,
+    kKBwdRecompute,
+    kKBwdDh,
+    kKBwdPrep,
+    kKBwdWgrad,
+    kKBwdDx,
     kNumKernelIds
 };
 

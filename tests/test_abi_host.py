@@ -28,7 +28,7 @@ def header_functions():
 def test_exports_every_declared_symbol(lib):
     import sparse_mixture_experts_gemv_amd._lib as b
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.SIGNATURES)
@@ -116,6 +116,24 @@ def test_parallel_linear_validation(lib):
     # fp32 rows [S*k, max(D_in, D_out)] + bf16 slot-order copies of x and g*dy + small tables
     base = 8192 * 14336 * 4 + 8192 * 4096 * 2 + 8192 * 14336 * 2
     assert base <= n <= base + (1 << 20)
+
+
+def test_ffn_bwd_validation(lib):
+    b = lib.moe_scatter_ffn_bwd
+    args = lambda S=16, D=64, F=128, E=8, k=2, ws=1 << 30, dx=FAKE, dg=FAKE, x=FAKE, tw=FAKE: (
+        x, FAKE, FAKE, FAKE, tw, FAKE, FAKE, FAKE, S, D, F, E, k, dx, FAKE, FAKE, FAKE, dg, FAKE, ws, None)
+    assert b(*args(k=9)) == 1
+    assert b(*args(x=None)) == 1
+    assert b(*args(tw=None)) == 1                 # the router weights are required
+    assert b(*args(dx=MISALIGNED)) == 1
+    assert b(*args(D=96)) == 2
+    assert b(*args(F=80)) == 2
+    assert b(*args(E=2048)) == 2
+    assert b(*args(ws=4096)) == 3
+    n = lib.moe_scatter_ffn_bwd_workspace_bytes(4096, 4096, 14336, 8, 2)
+    N = 8192
+    base = N * 2 * 14336 * 2 + N * 14336 * 2 + 2 * N * 4096 * 2 + N * 4096 * 4
+    assert base <= n <= base + N * 4 * 56 * 4 + (1 << 20)
 
 
 def test_workspace_has_no_token_replication(lib):
