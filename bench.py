@@ -11,6 +11,11 @@ roofline of the dominant kernel (timed live with HIP events on its own
 stream over the timed region) and the fp64 CPU oracle timed on a bounded
 sample of the same workload on this host.
 
+--op ffn_bwd times the backward of the expert FFN (moe_scatter_ffn_bwd: dx,
+dW1, dW3, dW2 and the router-weight gradient, with the gate+up forward
+recomputed inside) on the configuration's routing; its line reports the
+algorithmic backward TFLOP/s (12 S k D F, the recomputation not counted).
+
 --op pl_fwd / pl_bwd time the general ParallelLinear primitive instead, on
 the expert up-projection of the chosen configuration (x [S, D] read by
 index, W [E, D, F], router gates, output grouped [S*k, F]): the forward, or
@@ -209,6 +214,108 @@ def bench_parallel_linear(args, cfg, p):
     print(json.dumps(rec), flush=True)
 
 
+def ffn_bwd_cpu_baseline(cfg, p, ids, gates, target_s: float = 15.0):
+    """The fp64 oracle's FFN backward on a bounded sample of tokens (its weight gradients are
+    [E, D, F'] fp64 per call, so it runs on the first F' = 256 columns of F)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as wl
+
+    o = oracle.get()
+    order = np.random.default_rng(0).permutation(cfg.S)
+    Fs = min(cfg.F, 256)
+    w1 = wl.bf16_bits(p["w1"][:, :, :Fs].contiguous().cpu())
+    w3 = wl.bf16_bits(p["w3"][:, :, :Fs].contiguous().cpu())
+    w2 = wl.bf16_bits(p["w2"][:, :Fs, :].contiguous().cpu())
+    done, t_used, flops = 0, 0.0, 0.0
+    while t_used < target_s and done < cfg.S:
+        toks = np.sort(order[done:done + 2])
+        x = wl.bf16_bits(p["x"][torch.from_numpy(toks).to(p["x"].device)].cpu())
+        dout = wl.bf16_bits(torch.ones(toks.size, cfg.D, dtype=torch.bfloat16))
+        t0 = time.perf_counter()
+        o.ffn_bwd(x, w1, w3, w2, ids[toks], gates[toks].astype(np.float64), dout)
+        t_used += time.perf_counter() - t0
+        flops += 12.0 * toks.size * cfg.k * cfg.D * Fs
+        done += toks.size
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} random tokens of the {cfg.name} FFN backward (F {Fs} of {cfg.F}, fp64, 1 thread, "
+                      f"{t_used:.1f} s)"}
+
+
+def bench_ffn_bwd(args, cfg, p):
+    """moe_scatter_ffn_bwd with every output on the configuration's routing and a random dout."""
+    import torch
+
+    import sparse_mixture_experts_gemv_amd as smoe
+
+    S, D, F, E, k = cfg.S, cfg.D, cfg.F, cfg.E, cfg.k
+    if "ids" in p:
+        ids, gates = p["ids"], p["weights"]
+    else:
+        ids, gates = smoe.moe_route_topk(p["x"], p["wg"], k)
+    _, offsets, _, src = smoe.moe_sparse_map(ids, E)
+    ws = torch.empty(smoe.scatter_ffn_bwd_workspace_bytes(S, D, F, E, k), dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dout = (torch.randn((S, D), generator=g, device="cuda") * 0.1).to(torch.bfloat16)
+
+    def step():
+        smoe.moe_scatter_ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], gates, offsets, src, dout, workspace=ws)
+
+    N = S * k
+    flops = 12.0 * N * D * F
+    gemm_flops = {"bwd_recompute_gemm": 4.0 * N * D * F, "bwd_dh_gemm": 2.0 * N * D * F,
+                  "bwd_wgrad_gemm": 6.0 * N * D * F, "bwd_dx_gemm": 4.0 * N * D * F}
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    smoe.profile_start(args.steps * 24)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    kern = smoe.profile_stop()
+    ms = t0.elapsed_time(t1) / args.steps
+    # the GEMM kind with the most time per step (the weight gradients run as two launches per step)
+    per_step = {n: kern[n][0] / args.steps for n in gemm_flops if n in kern}
+    dominant = max(per_step, key=per_step.get)
+    achieved = gemm_flops[dominant] / (per_step[dominant] / 1e3) / 1e12
+    rec = {
+        "metric": "MoE expert-FFN backward TFLOP/s (dx, dW1, dW3, dW2, router-weight gradient)",
+        "value": round(flops / (ms / 1e3) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} expert FFN backward (SwiGLU, gate+up recomputed)", "S": S, "D": D,
+                   "F": F, "E": E, "k": k},
+        "tokens_per_s": round(S / (ms / 1e3), 1),
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_step": gemm_flops[dominant],
+                     "avg_step_us": round(per_step[dominant] * 1e3, 2)},
+        "kernels": {n: {"avg_us": round(1e3 * tot / c, 2), "launches": c} for n, (tot, c) in kern.items()},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 CPU oracle on a sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = ffn_bwd_cpu_baseline(cfg, p, ids.cpu().numpy(), gates.cpu().numpy(), args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,8 +325,9 @@ def main():
     ap.add_argument("--S", type=int, default=None, help="token count (default: the configuration's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="layer", choices=["layer", "pl_fwd", "pl_bwd"],
-                    help="layer: the MoE forward (default); pl_fwd / pl_bwd: ParallelLinear up-projection")
+    ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "pl_fwd", "pl_bwd"],
+                    help="layer: the MoE forward (default); ffn_bwd: the expert FFN backward; "
+                         "pl_fwd / pl_bwd: ParallelLinear up-projection")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run three device-to-device copies of BYTES (HBM counter calibration)")
     args = ap.parse_args()
@@ -256,6 +364,9 @@ def main():
     S, D, F, E, k = cfg.S, cfg.D, cfg.F, cfg.E, cfg.k
     print(f"bench: {cfg.describe()} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     p = wl.make_problem(cfg, S=S, device="cuda")
+    if args.op == "ffn_bwd":
+        bench_ffn_bwd(args, cfg, p)
+        return
     if args.op != "layer":
         bench_parallel_linear(args, cfg, p)
         return
