@@ -54,14 +54,20 @@ __global__ __launch_bounds__(256) void ffn_bwd_slot_rows_kernel(const uint4 *__r
     }
 }
 
-// dg[f] = sum over p of part[p * n + f], p = 0 .. nparts-1 in order.
+// dg[f] = sum over p of part[p * n + f]: a workgroup takes 64 routes (one per
+// lane); wave w sums the partials p = w, w + 4, ... in order and the four
+// wave sums are added in a fixed order, so the result is reproducible.
 __global__ __launch_bounds__(256) void ffn_bwd_gate_reduce_kernel(const float *__restrict__ part, int nparts, int n,
                                                                   float *__restrict__ dg) {
-    const int f = blockIdx.x * blockDim.x + threadIdx.x;
-    if (f >= n) return;
+    __shared__ float s_w[4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int f = blockIdx.x * 64 + lane;
     float s = 0.f;
-    for (int q = 0; q < nparts; ++q) s += part[(size_t)q * n + f];
-    dg[f] = s;
+    if (f < n)
+        for (int q = w; q < nparts; q += 4) s += part[(size_t)q * n + f];
+    s_w[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && f < n) dg[f] = (s_w[0][lane] + s_w[1][lane]) + (s_w[2][lane] + s_w[3][lane]);
 }
 
 static int bwd_pick_bm(int64_t avg) {
@@ -219,7 +225,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
 
     if (dg) {
         prof_begin(stream, kKBwdPrep);
-        ffn_bwd_gate_reduce_kernel<<<(N + 255) / 256, 256, 0, stream>>>(part, pl.nparts, N, dg);
+        ffn_bwd_gate_reduce_kernel<<<(N + 63) / 64, 256, 0, stream>>>(part, pl.nparts, N, dg);
         prof_end(stream, kKBwdPrep);
     }
 
@@ -246,9 +252,9 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
         q.E = E;
         q.ldb = D;
         q.n_mt = (F + 255) / 256;
-        q.n_nt = (D + 127) / 128;
+        q.n_nt = (D + 255) / 256;
         prof_begin(stream, kKBwdWgrad);
-        grouped_wgrad_kernel<256, 128, 1, 64, 2><<<device_cus(), 512, 0, stream>>>(q);
+        grouped_wgrad_kernel<256, 256, 1, 64, 2><<<device_cus(), 512, 0, stream>>>(q);
         prof_end(stream, kKBwdWgrad);
     }
     if (dw1 || dw3) {
@@ -264,12 +270,12 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
         q.N = F;
         q.E = E;
         q.ldb = 2 * F;
-        q.n_mt = (D + 127) / 128;
+        q.n_mt = (D + 255) / 256;
         q.n_nt = (F + 127) / 128;
         if (!dw1) q.B0 = ab + F;   // only dw3: both halves compute x^T db
         if (!dw3) q.B1 = ab;       // only dw1: both halves compute x^T da
         prof_begin(stream, kKBwdWgrad);
-        grouped_wgrad_kernel<128, 128, 2, 64, 3><<<device_cus(), 512, 0, stream>>>(q);
+        grouped_wgrad_kernel<256, 128, 2, 64, 2><<<device_cus(), 512, 0, stream>>>(q);
         prof_end(stream, kKBwdWgrad);
     }
 

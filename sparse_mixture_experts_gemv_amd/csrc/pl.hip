@@ -122,7 +122,7 @@ PlPlan pl_plan(int64_t S, int64_t k, int64_t D_in, int64_t D_out, int64_t E) {
     pl.n_ntiles_fwd = (int)((D_out + pl.bn - 1) / pl.bn);
     pl.n_ntiles_dx = (int)((D_in + pl.bn - 1) / pl.bn);
     pl.wg_bm = 256;
-    pl.wg_bn = 128;
+    pl.wg_bn = 256;
     pl.wg_mt = (int)((D_in + pl.wg_bm - 1) / pl.wg_bm);
     pl.wg_nt = (int)((D_out + pl.wg_bn - 1) / pl.wg_bn);
     const int nn = std::max(pl.n_ntiles_fwd, pl.n_ntiles_dx);
@@ -281,7 +281,7 @@ hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gate
         q.n_mt = pl.wg_mt;
         q.n_nt = pl.wg_nt;
         prof_begin(stream, kKPlWgrad);
-        grouped_wgrad_kernel<256, 128, 1, 64, 2><<<device_cus(), 512, 0, stream>>>(q);
+        grouped_wgrad_kernel<256, 256, 1, 64, 2><<<device_cus(), 512, 0, stream>>>(q);
         prof_end(stream, kKPlWgrad);
     }
     return hipGetLastError();
