@@ -88,15 +88,16 @@ hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gate
 
 // ---- expert FFN backward ----
 struct FfnBwdPlan {
-    int bm_r, bm_b, bn_b;        // tile rows of the recompute GEMM and of the dh / dx GEMMs; dh / dx tile columns
-    int nm_r, nm_b;              // M tiles (upper bounds)
+    int bm_r, bm_b, bm_x, bn_b;  // tile rows of the recompute, dh and dx GEMMs; dh tile columns
+    int nm_r, nm_b, nm_x;        // M tiles (upper bounds)
     int nn_r, nn_h, nn_x;        // N tiles of the recompute, dh and dx GEMMs
     int nparts;                  // router-gate partial sums per route
-    size_t tiles_r, tiles_b, order_r, order_h, order_x, counts, ab, h, dyg, xg, rows, part, ws_bytes;
+    size_t tiles_r, tiles_b, tiles_x, order_r, order_h, order_x, counts, ab, h, dyg, xg, rows, part, ws_bytes;
 };
 FfnBwdPlan ffn_bwd_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k);
 inline bool ffn_bwd_plan_fits(const FfnBwdPlan &pl) {
-    return pl.nm_r < (int)kOrderMtMask && pl.nm_b < (int)kOrderMtMask && pl.nn_r <= kOrderMaxNtiles &&
+    return pl.nm_r < (int)kOrderMtMask && pl.nm_b < (int)kOrderMtMask && pl.nm_x < (int)kOrderMtMask &&
+           pl.nn_r <= kOrderMaxNtiles &&
            pl.nn_h <= kOrderMaxNtiles && pl.nn_x <= kOrderMaxNtiles;
 }
 hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,

@@ -2,7 +2,7 @@
 
 Small shapes are compared element by element (every gradient, every
 element); they cover each tile height of the recompute GEMM (256, 192, 64 and
-32 rows) and of the backward GEMMs (128, 64, 32), ragged tiles (D or F not a
+32 rows) and of the backward GEMMs (192, 128, 64, 32), ragged tiles (D or F not a
 multiple of 256), k = 1, empty experts (zero weight gradients) and skewed
 routing. Full-size configurations are checked on samples the oracle can
 compute: dx and the router-weight gradient of sampled tokens, and 64-column
@@ -28,7 +28,8 @@ from gpu_util import DEV, bf16_floor_mae, say
 
 pytestmark = pytest.mark.gpu
 
-SMALL = [  # (S, D, F, E, k, skew): recompute tile from S*k/E (256/192/64/32), backward tile (128/64/32)
+SMALL = [  # (S, D, F, E, k, skew): recompute tile from S*k/E (256/192/64/32), dh / dx tiles (192/128/64/32)
+    (1000, 128, 192, 4, 2, None),   # 500 rows per expert: 256 / 128 (dh) and 192 (dx)
     (1000, 192, 320, 8, 2, None),   # 250 rows per expert: 256 / 128; F and D ragged against 256
     (600, 128, 192, 8, 2, None),    # 150: 192 / 128
     (300, 128, 192, 8, 2, None),    # 75: 64 / 64
