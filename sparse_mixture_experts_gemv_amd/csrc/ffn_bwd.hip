@@ -70,13 +70,17 @@ __global__ __launch_bounds__(256) void ffn_bwd_gate_reduce_kernel(const float *_
     if (w == 0 && f < n) dg[f] = (s_w[0][lane] + s_w[1][lane]) + (s_w[2][lane] + s_w[3][lane]);
 }
 
+// Tile rows of the dh GEMM: 192 for experts of ~100-190 rows (one tile per
+// expert, so its W2 streams once; the short-tile path skips missing rows),
+// else 128 / 64 / 32.
 static int bwd_pick_bm(int64_t avg) {
-    if (avg >= 96) return 128;
+    if (avg >= 192) return 128;
+    if (avg >= 96) return 192;
     if (avg >= 48) return 64;
     return 32;
 }
 
-// The input-gradient GEMM (K = 2F) takes 192-row tiles once experts are
+// The input-gradient GEMM (K = 2F) also takes 192-row tiles once experts are
 // large (measured on Mixtral: 1.82 against 2.13 ms with 128-row tiles, while
 // the dh GEMM, K = D, is faster with 128 rows).
 static int bwd_pick_bm_dx(int64_t avg) { return avg >= 384 ? 192 : bwd_pick_bm(avg); }
@@ -139,11 +143,15 @@ static void launch_recompute(int bm, const GemmParams &p, hipStream_t stream) {
     }
 }
 
-// one transposed weight, 256-column tiles (128 for 32-row tiles)
+// one transposed weight, 256-column tiles (128 for 32-row tiles); 192-row
+// tiles over experts shorter than the tile take the short-tile path
 template <int MODE, int FLAGS>
-static void launch_bwd_bt(int bm, const GemmParams &p, hipStream_t stream) {
+static void launch_bwd_bt(int bm, int64_t avg, const GemmParams &p, hipStream_t stream) {
     switch (bm) {
-        case 192: bwd_tile<192, 256, MODE, 64, 3, 2, false, FLAGS>(p, stream); break;
+        case 192:
+            if (avg < 192) bwd_tile<192, 256, MODE, 64, 3, 2, true, FLAGS>(p, stream);
+            else bwd_tile<192, 256, MODE, 64, 3, 2, false, FLAGS>(p, stream);
+            break;
         case 128: bwd_tile<128, 256, MODE, 64, 4, 2, false, FLAGS>(p, stream); break;
         case 64: bwd_tile<64, 256, MODE, 64, 3, 3, false, FLAGS>(p, stream); break;
         default: bwd_tile<32, 128, MODE, 64, 4, 4, false, FLAGS>(p, stream); break;
@@ -231,7 +239,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
     p.N = F;
     p.K = D;
     prof_begin(stream, kKBwdDh);
-    launch_bwd_bt<kSwigluBwd, kFlagBT>(pl.bm_b, p, stream);
+    launch_bwd_bt<kSwigluBwd, kFlagBT>(pl.bm_b, (int64_t)N / E, p, stream);
     prof_end(stream, kKBwdDh);
 
     if (dg) {
@@ -306,7 +314,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
         p.N = D;
         p.K = 2 * F;
         prof_begin(stream, kKBwdDx);
-        launch_bwd_bt<kDownRows, kFlagBT | kFlagKSplit>(pl.bm_x, p, stream);
+        launch_bwd_bt<kDownRows, kFlagBT | kFlagKSplit>(pl.bm_x, (int64_t)N / E, p, stream);
         prof_end(stream, kKBwdDx);
         launch_combine_rows(rows, dx, S, D, k, stream);
     }
