@@ -106,9 +106,14 @@ __global__ __launch_bounds__(256) void pl_finalize_kernel(const float *__restric
 }
 
 // Tile heights of the ParallelLinear GEMMs (one weight matrix, 256-column
-// tiles; the forward and input-gradient GEMMs share the tile table).
+// tiles; the forward and input-gradient GEMMs share the tile table): 192
+// rows for large experts, 128 rows for ~190-380 rows per expert, 192 rows on
+// the short-tile path for ~100-190 (one tile per expert, so its weights
+// stream once), then 64 and 32.
 static int pl_pick_bm(int64_t avg) {
-    if (avg >= 96) return 128;
+    if (avg >= 384) return 192;
+    if (avg >= 192) return 128;
+    if (avg >= 96) return 192;
     if (avg >= 48) return 64;
     return 32;
 }
@@ -143,18 +148,22 @@ PlPlan pl_plan(int64_t S, int64_t k, int64_t D_in, int64_t D_out, int64_t E) {
     return pl;
 }
 
-template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A, int FLAGS>
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A, int FLAGS, bool SKIP = false>
 static void launch_pl_tile(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
     p.n_ntiles = (p.N + BN - 1) / BN;
     if (p.n_mtiles * p.n_ntiles == 0) return;
-    grouped_gemm_pp_persistent_kernel<BM, BN, MODE, BK, STAGES, STAGES_A, false, FLAGS>
+    grouped_gemm_pp_persistent_kernel<BM, BN, MODE, BK, STAGES, STAGES_A, SKIP, FLAGS>
         <<<device_cus(), 512, 0, stream>>>(p);
 }
 
 template <int MODE, int FLAGS>
-static void launch_pl_gemm(int bm, const GemmParams &p, hipStream_t stream) {
+static void launch_pl_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t stream) {
     switch (bm) {
+        case 192:
+            if (avg < 192) launch_pl_tile<192, 256, MODE, 64, 3, 2, FLAGS, true>(p, stream);
+            else launch_pl_tile<192, 256, MODE, 64, 3, 2, FLAGS, false>(p, stream);
+            break;
         case 128: launch_pl_tile<128, 256, MODE, 64, 4, 2, FLAGS>(p, stream); break;
         case 64: launch_pl_tile<64, 256, MODE, 64, 3, 3, FLAGS>(p, stream); break;
         default: launch_pl_tile<32, 128, MODE, 64, 4, 4, FLAGS>(p, stream); break;
@@ -206,10 +215,10 @@ hipError_t launch_pl_fwd(const uint16_t *x, const uint16_t *w, const float *gate
     prof_begin(stream, kKPlGemm);
     if (grouped_out) {
         p.C = y;
-        launch_pl_gemm<kLinBf16, 0>(pl.bm, p, stream);
+        launch_pl_gemm<kLinBf16, 0>(pl.bm, (int64_t)N / E, p, stream);
     } else {
         p.C = ws + pl.rows_off;
-        launch_pl_gemm<kDownRows, 0>(pl.bm, p, stream);
+        launch_pl_gemm<kDownRows, 0>(pl.bm, (int64_t)N / E, p, stream);
     }
     prof_end(stream, kKPlGemm);
     if (!grouped_out) launch_combine_rows(reinterpret_cast<const float *>(ws + pl.rows_off), y, S, D_out, k, stream);
@@ -236,7 +245,7 @@ hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gate
         p.N = D_in;
         p.C = ws + pl.rows_off;
         prof_begin(stream, kKPlDxGemm);
-        launch_pl_gemm<kDownRows, kFlagBT>(pl.bm, p, stream);
+        launch_pl_gemm<kDownRows, kFlagBT>(pl.bm, (int64_t)N / E, p, stream);
         prof_end(stream, kKPlDxGemm);
         const float *c = reinterpret_cast<const float *>(ws + pl.rows_off);
         prof_begin(stream, kKPlFinalize);

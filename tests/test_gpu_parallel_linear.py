@@ -1,8 +1,8 @@
 """moe_parallel_linear_fwd / moe_parallel_linear_bwd on the GPU against the fp64 oracle.
 
 Every grouping mode (grouped or scattered input and output), with and
-without router gates, on shapes that cover each M-tile height (128, 64 and
-32 rows), ragged N tiles (D_in or D_out not a multiple of 256), k = 1, many
+without router gates, on shapes that cover each M-tile height (192 full
+and short, 128, 64 and 32 rows), ragged N tiles (D_in or D_out not a multiple of 256), k = 1, many
 empty experts (whose weight gradient must be exactly zero) and skewed
 routing. Outputs are compared element by element with the tolerance bar of
 the forward pass; the weight gradient is fp32 and is compared the same way
@@ -19,7 +19,9 @@ pytestmark = pytest.mark.gpu
 
 MODES = [(False, False), (False, True), (True, False), (True, True)]
 SHAPES = [  # (S, k, D_in, D_out, E, skew)
-    (700, 2, 256, 320, 8, None),   # 175 rows per expert: 128-row tiles; D_out ragged against 256 columns
+    (1000, 2, 128, 192, 4, None),  # 500 rows per expert: 192-row tiles
+    (1000, 2, 128, 256, 8, None),  # 250: 128-row tiles
+    (700, 2, 256, 320, 8, None),   # 175: 192-row tiles on the short-tile path; D_out ragged against 256 columns
     (300, 2, 192, 128, 8, None),   # 75: 64-row tiles; D_in ragged
     (120, 2, 128, 192, 16, 1.2),   # 15: 32-row tiles, skewed routing
     (65, 1, 64, 64, 4, None),      # k = 1
