@@ -67,41 +67,87 @@ __global__ __launch_bounds__(256) void pl_slot_rows_kernel(const uint4 *__restri
 //       dx[t] = bf16(sum_j g_f c_f) (j in order), dg[f] = <x[t], c_f>
 //   grouped input: one workgroup per slot r, f = slot_src[r]:
 //       dx[r] = bf16(g_f c_f), dg[f] = <x[r], c_f>
-// dx or dg may be NULL; a NULL gate means 1. The dot products use a fixed
-// per-thread column split and a fixed tree, so they are reproducible.
+// dx or dg may be NULL; a NULL gate means 1. One pass over the rows for up
+// to kPlChunk routes per token (more are taken in chunks, dx then in a pass
+// of its own); each thread owns fixed groups of 4 columns and the dot
+// products are reduced in a fixed order, so results are reproducible.
+constexpr int kPlChunk = 16;
+
+__device__ __forceinline__ float pl_block_sum(float v, float *s_w) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) s_w[w] = v;
+    __syncthreads();
+    return (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+}
+
 template <bool GROUPED>
-__global__ __launch_bounds__(256) void pl_finalize_kernel(const float *__restrict__ c, const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(256) void pl_finalize_kernel(const float4 *__restrict__ c, const uint2 *__restrict__ x,
                                                           const int32_t *__restrict__ slot_src,
-                                                          const float *__restrict__ gate, int k, int D,
-                                                          uint16_t *__restrict__ dx, float *__restrict__ dg) {
-    __shared__ float s_red[256];
+                                                          const float *__restrict__ gate, int k, int D4,
+                                                          uint2 *__restrict__ dx, float *__restrict__ dg) {
+    __shared__ float s_w[4];
     const int item = blockIdx.x;  // token (scattered) or slot (grouped)
     const int nr = GROUPED ? 1 : k;
     const int f0 = GROUPED ? slot_src[item] : item * k;
-    if (dx) {
-        for (int d = threadIdx.x; d < D; d += 256) {
-            float s = 0.f;
-            for (int j = 0; j < nr; ++j) {
-                const int f = f0 + j;
-                s += (gate ? gate[f] : 1.0f) * c[(size_t)f * D + d];
+    const bool fused_dx = dx != nullptr && nr <= kPlChunk;
+    const uint2 *xr = x + (size_t)item * D4;
+    for (int j0 = 0; j0 < nr; j0 += kPlChunk) {
+        const int nj = min(kPlChunk, nr - j0);
+        float g[kPlChunk], dot[kPlChunk];
+#pragma unroll
+        for (int j = 0; j < kPlChunk; ++j) {
+            g[j] = (j < nj && gate) ? gate[f0 + j0 + j] : 1.0f;
+            dot[j] = 0.f;
+        }
+        for (int d = threadIdx.x; d < D4; d += 256) {
+            const uint2 xv = xr[d];
+            const float x0 = bf16_bits_to_f32(xv.x & 0xffffu), x1 = bf16_bits_to_f32(xv.x >> 16);
+            const float x2 = bf16_bits_to_f32(xv.y & 0xffffu), x3 = bf16_bits_to_f32(xv.y >> 16);
+            float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < kPlChunk; ++j) {
+                if (j < nj) {
+                    const float4 cv = c[(size_t)(f0 + j0 + j) * D4 + d];
+                    s.x += g[j] * cv.x;
+                    s.y += g[j] * cv.y;
+                    s.z += g[j] * cv.z;
+                    s.w += g[j] * cv.w;
+                    dot[j] += ((x0 * cv.x + x1 * cv.y) + (x2 * cv.z + x3 * cv.w));
+                }
             }
-            dx[(size_t)item * D + d] = f32_to_bf16_bits(s);
+            if (fused_dx) {
+                const uint32_t lo = (uint32_t)f32_to_bf16_bits(s.x) | ((uint32_t)f32_to_bf16_bits(s.y) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16_bits(s.z) | ((uint32_t)f32_to_bf16_bits(s.w) << 16);
+                dx[(size_t)item * D4 + d] = make_uint2(lo, hi);
+            }
+        }
+        if (dg) {
+#pragma unroll
+            for (int j = 0; j < kPlChunk; ++j) {
+                if (j < nj) {
+                    const float v = pl_block_sum(dot[j], s_w);
+                    if (threadIdx.x == 0) dg[f0 + j0 + j] = v;
+                }
+            }
         }
     }
-    if (!dg) return;
-    const uint16_t *xr = x + (size_t)item * D;
-    for (int j = 0; j < nr; ++j) {
-        const int f = f0 + j;
-        float dot = 0.f;
-        for (int d = threadIdx.x; d < D; d += 256) dot += bf16_bits_to_f32(xr[d]) * c[(size_t)f * D + d];
-        s_red[threadIdx.x] = dot;
-        __syncthreads();
-        for (int w = 128; w > 0; w >>= 1) {
-            if ((int)threadIdx.x < w) s_red[threadIdx.x] += s_red[threadIdx.x + w];
-            __syncthreads();
+    if (dx && !fused_dx) {
+        for (int d = threadIdx.x; d < D4; d += 256) {
+            float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 0; j < nr; ++j) {
+                const float gj = gate ? gate[f0 + j] : 1.0f;
+                const float4 cv = c[(size_t)(f0 + j) * D4 + d];
+                s.x += gj * cv.x;
+                s.y += gj * cv.y;
+                s.z += gj * cv.z;
+                s.w += gj * cv.w;
+            }
+            const uint32_t lo = (uint32_t)f32_to_bf16_bits(s.x) | ((uint32_t)f32_to_bf16_bits(s.y) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16_bits(s.z) | ((uint32_t)f32_to_bf16_bits(s.w) << 16);
+            dx[(size_t)item * D4 + d] = make_uint2(lo, hi);
         }
-        if (threadIdx.x == 0) dg[f] = s_red[0];
-        __syncthreads();
     }
 }
 
@@ -247,12 +293,14 @@ hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gate
         prof_begin(stream, kKPlDxGemm);
         launch_pl_gemm<kDownRows, kFlagBT>(pl.bm, (int64_t)N / E, p, stream);
         prof_end(stream, kKPlDxGemm);
-        const float *c = reinterpret_cast<const float *>(ws + pl.rows_off);
+        const float4 *c = reinterpret_cast<const float4 *>(ws + pl.rows_off);
+        const uint2 *x4 = reinterpret_cast<const uint2 *>(x);
+        uint2 *dx4 = reinterpret_cast<uint2 *>(dx);
         prof_begin(stream, kKPlFinalize);
         if (grouped_in) {
-            if (N > 0) pl_finalize_kernel<true><<<N, 256, 0, stream>>>(c, x, slot_src, gates, k, D_in, dx, dgates);
+            if (N > 0) pl_finalize_kernel<true><<<N, 256, 0, stream>>>(c, x4, slot_src, gates, k, D_in / 4, dx4, dgates);
         } else {
-            if (S > 0) pl_finalize_kernel<false><<<S, 256, 0, stream>>>(c, x, slot_src, gates, k, D_in, dx, dgates);
+            if (S > 0) pl_finalize_kernel<false><<<S, 256, 0, stream>>>(c, x4, slot_src, gates, k, D_in / 4, dx4, dgates);
         }
         prof_end(stream, kKPlFinalize);
     }
