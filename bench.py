@@ -16,6 +16,10 @@ dW1, dW3, dW2 and the router-weight gradient, with the gate+up forward
 recomputed inside) on the configuration's routing; its line reports the
 algorithmic backward TFLOP/s (12 S k D F, the recomputation not counted).
 
+--op map_sweep times the sparse map alone on the ids of the top-4 of iid
+N(0, 1) logits over 128 experts, S in {2^13, 2^16, 2^19, 2^21} (median of
+20 launches each), against its algorithmic bytes 12 S k + 8 E.
+
 --op pl_fwd / pl_bwd time the general ParallelLinear primitive instead, on
 the expert up-projection of the chosen configuration (x [S, D] read by
 index, W [E, D, F], router gates, output grouped [S*k, F]): the forward, or
@@ -316,6 +320,50 @@ def bench_ffn_bwd(args, cfg, p):
     print(json.dumps(rec), flush=True)
 
 
+def bench_map_sweep(args):
+    """The sparse map alone: ids = top-4 of iid N(0, 1) logits [S, 128] (drawn on the GPU, not timed)."""
+    import torch
+
+    import sparse_mixture_experts_gemv_amd as smoe
+
+    E, k = 128, 4
+    rows = []
+    for lg in (13, 16, 19, 21):
+        S = 1 << lg
+        g = torch.Generator(device="cuda").manual_seed(lg)
+        ids = torch.randn((S, E), generator=g, device="cuda").topk(k, dim=1).indices.to(torch.int32).contiguous()
+        out = (torch.empty(E, dtype=torch.int32, device="cuda"), torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+               torch.empty(S * k, dtype=torch.int32, device="cuda"), torch.empty(S * k, dtype=torch.int32, device="cuda"))
+        ws = torch.empty(smoe.sparse_map_workspace_bytes(S, k, E), dtype=torch.uint8, device="cuda")
+        for _ in range(5):
+            smoe.moe_sparse_map(ids, E, out, ws)
+        times = []
+        for _ in range(20):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            smoe.moe_sparse_map(ids, E, out, ws)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        us = sorted(times)[len(times) // 2]
+        smoe.profile_start(64)
+        for _ in range(10):
+            smoe.moe_sparse_map(ids, E, out, ws)
+        kern = smoe.profile_stop()
+        nbytes = 12.0 * S * k + 8.0 * E
+        rows.append({"S": S, "median_us": round(us, 2), "GB_s": round(nbytes / us / 1e3, 1),
+                     "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                     "kernels_us": {n: round(1e3 * tot / c, 2) for n, (tot, c) in kern.items()}})
+    big = rows[-1]
+    rec = {"metric": "sparse map bandwidth (ids from top-4 of N(0,1) logits, E = 128)", "value": big["GB_s"],
+           "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "int32", "data": "synthetic",
+           "config": {"workload": "sparse map alone, E = 128, k = 4, S = 2^13 .. 2^21"},
+           "roofline": {"kernel": "sparse map (3 launches)", "bound": "hbm", "achieved": big["GB_s"],
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": big["hbm_frac"], "traffic": None},
+           "sweep": rows}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,7 +373,7 @@ def main():
     ap.add_argument("--S", type=int, default=None, help="token count (default: the configuration's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "pl_fwd", "pl_bwd"],
+    ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "pl_fwd", "pl_bwd", "map_sweep"],
                     help="layer: the MoE forward (default); ffn_bwd: the expert FFN backward; "
                          "pl_fwd / pl_bwd: ParallelLinear up-projection")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -357,6 +405,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n * 4, "launches": 3}))
+        return
+    if args.op == "map_sweep":
+        bench_map_sweep(args)
         return
     cfg = wl.CONFIGS[args.config]
     if args.S:

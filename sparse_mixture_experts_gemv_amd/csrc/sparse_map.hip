@@ -20,6 +20,8 @@
 //   pass 1 (hist):    per sub-chunk counts  -> cnt[e][sub]       (workspace)
 //   pass 2 (rowscan): per expert, exclusive scan over sub-chunks, total
 //   pass 3 (assign):  offsets from the totals, then rank -> slot
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "profile.hpp"
@@ -28,6 +30,7 @@ namespace smoe {
 
 constexpr int kMapWaves = 4;
 constexpr int kMaxExperts = 1024;
+constexpr int kMapUnroll = 4;  // groups of 64 routes whose ids are loaded together
 
 __device__ __forceinline__ unsigned long long match_any(int key, int nbits) {
     unsigned long long m = __ballot(1);
@@ -49,13 +52,21 @@ __global__ __launch_bounds__(256) void smap_hist_kernel(const int32_t *__restric
     __syncthreads();
     if (sub < nsub) {
         const int base = sub * L;
-        for (int g = 0; g < L; g += 64) {
-            const int f = base + g + lane;
-            int e = f < N ? ids[f] : E;  // E = sentinel: lanes past the end, ids outside [0, E)
-            if ((unsigned)e >= (unsigned)E) e = E;
-            const unsigned long long m = match_any(e, nbits);
-            const int leader = __ffsll(m) - 1;
-            if (lane == leader && e < E) my[e] += __popcll(m);
+        for (int g0 = 0; g0 < L; g0 += 64 * kMapUnroll) {
+            int ev[kMapUnroll];  // the ids of kMapUnroll groups are loaded before any is used
+#pragma unroll
+            for (int u = 0; u < kMapUnroll; ++u) {
+                const int f = base + g0 + 64 * u + lane;
+                ev[u] = f < N ? ids[f] : E;  // E = sentinel: lanes past the end, ids outside [0, E)
+            }
+#pragma unroll
+            for (int u = 0; u < kMapUnroll; ++u) {
+                int e = ev[u];
+                if ((unsigned)e >= (unsigned)E) e = E;
+                const unsigned long long m = match_any(e, nbits);
+                const int leader = __ffsll(m) - 1;
+                if (lane == leader && e < E) my[e] += __popcll(m);
+            }
         }
         for (int e = lane; e < E; e += 64) cnt[(size_t)e * nsub + sub] = my[e];
     }
@@ -156,22 +167,31 @@ __global__ __launch_bounds__(256) void smap_assign_kernel(const int32_t *__restr
     for (int e = lane; e < E; e += 64) my[e] = s_off[e] + cnt[(size_t)e * nsub + sub];
     const int base = sub * L;
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int g = 0; g < L; g += 64) {
-        const int f = base + g + lane;
-        int e = f < N ? ids[f] : E;
-        if ((unsigned)e >= (unsigned)E) e = E;
-        const unsigned long long m = match_any(e, nbits);
-        const int leader = __ffsll(m) - 1;
-        int b = (lane == leader && e < E) ? my[e] : 0;
-        b = __shfl(b, leader);
-        if (e < E) {
-            const int slot = b + __popcll(m & lt);
-            sparse_rows[f] = slot;
-            slot_src[slot] = f;
-        } else if (f < N) {
-            sparse_rows[f] = -1;  // id outside [0, E): the route gets no slot
+    for (int g0 = 0; g0 < L; g0 += 64 * kMapUnroll) {
+        int ev[kMapUnroll];
+#pragma unroll
+        for (int u = 0; u < kMapUnroll; ++u) {
+            const int f = base + g0 + 64 * u + lane;
+            ev[u] = f < N ? ids[f] : E;
         }
-        if (lane == leader && e < E) my[e] = b + __popcll(m);
+#pragma unroll
+        for (int u = 0; u < kMapUnroll; ++u) {
+            const int f = base + g0 + 64 * u + lane;
+            int e = ev[u];
+            if ((unsigned)e >= (unsigned)E) e = E;
+            const unsigned long long m = match_any(e, nbits);
+            const int leader = __ffsll(m) - 1;
+            int b = (lane == leader && e < E) ? my[e] : 0;
+            b = __shfl(b, leader);
+            if (e < E) {
+                const int slot = b + __popcll(m & lt);
+                sparse_rows[f] = slot;
+                slot_src[slot] = f;
+            } else if (f < N) {
+                sparse_rows[f] = -1;  // id outside [0, E): the route gets no slot
+            }
+            if (lane == leader && e < E) my[e] = b + __popcll(m);
+        }
     }
 }
 
@@ -184,8 +204,13 @@ __global__ void smap_empty_kernel(int E, int32_t *expert_counts, int32_t *expert
 
 SparseMapPlan sparse_map_plan(int64_t N, int E) {
     SparseMapPlan pl;
+    // sub-chunks of L = 256 * 2^j routes (a multiple of 64 * kMapUnroll); up
+    // to max(2048, 2^20 / E) of them, so large maps keep many waves busy (a
+    // wave's loop over its L routes is latency-bound) while the per-sub-chunk
+    // count matrix stays within 4 MB
+    const int64_t max_sub = std::max<int64_t>(2048, ((int64_t)1 << 20) / std::max(E, 1));
     int64_t L = 256;
-    while (N / L > 2048) L *= 2;
+    while ((N + L - 1) / L > max_sub) L *= 2;
     pl.L = (int)L;
     pl.nsub = (int)((N + L - 1) / L);
     pl.nbits = 32 - __builtin_clz((unsigned)E);  // bits to hold 0..E (E is the sentinel)
