@@ -212,26 +212,49 @@ __device__ __forceinline__ void wg_tile(const WgradParams &p, char *smem, int e,
     if (group == 0) pp_barrier();
 #undef SMOE_WG_ISSUE
 
-    // epilogue: lane holds column lane % 16 and rows 4 (lane / 16) + r of each 16x16 block
+    // Epilogue through LDS (the ring is free once every wave is past the
+    // loop): each wave writes a slice of its accumulators to its own LDS
+    // region in the MFMA layout (lane holds column lane % 16 and rows
+    // 4 (lane / 16) + r of a 16x16 block) and reads it back as rows, so the
+    // fp32 gradient leaves in 16-byte stores covering WTN-column row
+    // segments (128 or 256 bytes) instead of 64-byte pieces of four rows.
+    constexpr int STRIDE = WTN + 4;  // floats per LDS row (+4: distinct banks for the 4 row groups)
+    constexpr int WAVE_BYTES_FULL = MT * 16 * STRIDE * 4;
+    constexpr int LDS_BYTES = WgGeom<BM, BN, NB, BK, STAGES>::SMEM;
+    constexpr int PASSES = (8 * WAVE_BYTES_FULL <= LDS_BYTES) ? 1 : (8 * WAVE_BYTES_FULL / 2 <= LDS_BYTES) ? 2 : 4;
+    static_assert(MT % PASSES == 0 && 8 * (WAVE_BYTES_FULL / PASSES) <= LDS_BYTES, "epilogue staging fits the ring");
+    constexpr int MT_P = MT / PASSES;          // 16-row blocks per pass
+    constexpr int ROWS_P = MT_P * 16;          // LDS rows per wave per pass
+    constexpr int LANES_PER_ROW = WTN / 4;     // 16-byte pieces per row
+    constexpr int ROWS_PER_READ = 64 / LANES_PER_ROW;
+    float *reg = reinterpret_cast<float *>(smem) + wave * (ROWS_P * STRIDE);
     const int col_in_tile = lane & 15;
     const int row_grp = (lane >> 4) * 4;
+    const int rd_row = lane / LANES_PER_ROW, rd_col = (lane % LANES_PER_ROW) * 4;
+    __syncthreads();  // every wave is done reading the operand ring
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         float *C = (b == 0 ? p.C0 : p.C1) + (size_t)e * M * N;
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + (WM * i + wm) * 16 + row_grp + r;
-                if (m >= M) continue;
-                float *row = C + (size_t)m * N + n0;
+            for (int il = 0; il < MT_P; ++il)
 #pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const int col = wn * WTN + j * 16 + col_in_tile;
-                    if (n0 + col < N) row[col] = acc[b][i][j][r];
-                }
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        reg[(il * 16 + row_grp + r) * STRIDE + j * 16 + col_in_tile] = acc[b][ps * MT_P + il][j][r];
+#pragma unroll
+            for (int q = 0; q < ROWS_P / ROWS_PER_READ; ++q) {
+                const int rl = q * ROWS_PER_READ + rd_row;  // LDS row: block il = rl / 16, row rl % 16
+                const int m = m0 + (WM * (ps * MT_P + rl / 16) + wm) * 16 + (rl % 16);
+                const int n = n0 + wn * WTN + rd_col;
+                const float4 v = *reinterpret_cast<const float4 *>(reg + rl * STRIDE + rd_col);
+                if (m < M && n < N) *reinterpret_cast<float4 *>(C + (size_t)m * N + n) = v;
             }
+        }
     }
+    __syncthreads();  // the next tile's DMA may overwrite the staging area
 }
 
 // Persistent: one workgroup per CU walks the tiles (expert major, then N
