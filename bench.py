@@ -16,6 +16,11 @@ dW1, dW3, dW2 and the router-weight gradient, with the gate+up forward
 recomputed inside) on the configuration's routing; its line reports the
 algorithmic backward TFLOP/s (12 S k D F, the recomputation not counted).
 
+--op train times one training step of the layer's experts on the
+configuration's routing: the training-mode forward (which keeps a, b and h)
+followed by the backward fed those activations (no recomputation);
+algorithmic 18 S k D F FLOP (forward 6, backward 12).
+
 --op map_sweep times the sparse map alone on the ids of the top-4 of iid
 N(0, 1) logits over 128 experts, S in {2^13, 2^16, 2^19, 2^21} (median of
 20 launches each), against its algorithmic bytes 12 S k + 8 E.
@@ -248,8 +253,9 @@ def ffn_bwd_cpu_baseline(cfg, p, ids, gates, target_s: float = 15.0):
                       f"{t_used:.1f} s)"}
 
 
-def bench_ffn_bwd(args, cfg, p):
-    """moe_scatter_ffn_bwd with every output on the configuration's routing and a random dout."""
+def bench_ffn_bwd(args, cfg, p, train=False):
+    """moe_scatter_ffn_bwd with every output on the configuration's routing and a random dout;
+    with train, each step is the training-mode forward plus the backward on its saved activations."""
     import torch
 
     import sparse_mixture_experts_gemv_amd as smoe
@@ -264,13 +270,24 @@ def bench_ffn_bwd(args, cfg, p):
     g = torch.Generator(device="cuda").manual_seed(7)
     dout = (torch.randn((S, D), generator=g, device="cuda") * 0.1).to(torch.bfloat16)
 
-    def step():
-        smoe.moe_scatter_ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], gates, offsets, src, dout, workspace=ws)
+    if train:
+        saved = torch.empty(smoe.saved_activations_numel(S, F, k), dtype=torch.bfloat16, device="cuda")
+        fws = torch.empty(smoe.scatter_ffn_workspace_bytes(S, D, F, E, k), dtype=torch.uint8, device="cuda")
+        out = torch.empty((S, D), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            smoe.moe_scatter_ffn_fwd(p["x"], p["w1"], p["w3"], p["w2"], gates, offsets, src, out, fws, saved=saved)
+            smoe.moe_scatter_ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], gates, offsets, src, dout, workspace=ws,
+                                     saved=saved)
+    else:
+        def step():
+            smoe.moe_scatter_ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], gates, offsets, src, dout, workspace=ws)
 
     N = S * k
-    flops = 12.0 * N * D * F
+    flops = (18.0 if train else 12.0) * N * D * F
     gemm_flops = {"bwd_recompute_gemm": 4.0 * N * D * F, "bwd_dh_gemm": 2.0 * N * D * F,
-                  "bwd_wgrad_gemm": 6.0 * N * D * F, "bwd_dx_gemm": 4.0 * N * D * F}
+                  "bwd_wgrad_gemm": 6.0 * N * D * F, "bwd_dx_gemm": 4.0 * N * D * F,
+                  "ffn_gate_up_gemm": 4.0 * N * D * F, "ffn_down_scatter_gemm": 2.0 * N * D * F}
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         step()
@@ -292,7 +309,8 @@ def bench_ffn_bwd(args, cfg, p):
     dominant = max(per_step, key=per_step.get)
     achieved = gemm_flops[dominant] / (per_step[dominant] / 1e3) / 1e12
     rec = {
-        "metric": "MoE expert-FFN backward TFLOP/s (dx, dW1, dW3, dW2, router-weight gradient)",
+        "metric": ("MoE expert-FFN training step TFLOP/s (forward keeping activations + backward)" if train else
+                   "MoE expert-FFN backward TFLOP/s (dx, dW1, dW3, dW2, router-weight gradient)"),
         "value": round(flops / (ms / 1e3) / 1e12, 1),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -304,8 +322,9 @@ def bench_ffn_bwd(args, cfg, p):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name} expert FFN backward (SwiGLU, gate+up recomputed)", "S": S, "D": D,
-                   "F": F, "E": E, "k": k},
+        "config": {"workload": (f"{cfg.name} expert FFN training step (forward + backward, saved activations)"
+                                if train else f"{cfg.name} expert FFN backward (SwiGLU, gate+up recomputed)"),
+                   "S": S, "D": D, "F": F, "E": E, "k": k},
         "tokens_per_s": round(S / (ms / 1e3), 1),
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
@@ -314,7 +333,7 @@ def bench_ffn_bwd(args, cfg, p):
         "kernels": {n: {"avg_us": round(1e3 * tot / c, 2), "launches": c} for n, (tot, c) in kern.items()},
         "wall_s_timed_region": round(wall, 3),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not train:
         print("bench: timing the fp64 CPU oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = ffn_bwd_cpu_baseline(cfg, p, ids.cpu().numpy(), gates.cpu().numpy(), args.cpu_seconds)
     print(json.dumps(rec), flush=True)
@@ -373,7 +392,7 @@ def main():
     ap.add_argument("--S", type=int, default=None, help="token count (default: the configuration's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "pl_fwd", "pl_bwd", "map_sweep"],
+    ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "train", "pl_fwd", "pl_bwd", "map_sweep"],
                     help="layer: the MoE forward (default); ffn_bwd: the expert FFN backward; "
                          "pl_fwd / pl_bwd: ParallelLinear up-projection")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -415,8 +434,8 @@ def main():
     S, D, F, E, k = cfg.S, cfg.D, cfg.F, cfg.E, cfg.k
     print(f"bench: {cfg.describe()} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     p = wl.make_problem(cfg, S=S, device="cuda")
-    if args.op == "ffn_bwd":
-        bench_ffn_bwd(args, cfg, p)
+    if args.op in ("ffn_bwd", "train"):
+        bench_ffn_bwd(args, cfg, p, train=args.op == "train")
         return
     if args.op != "layer":
         bench_parallel_linear(args, cfg, p)

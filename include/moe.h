@@ -173,6 +173,22 @@ int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Training-mode forward: moe_scatter_ffn_fwd with the per-route-rows combine
+ * that also keeps, for the backward, the gate and up projections a and b of
+ * every slot (bf16, rounded from the fp32 sums) and h (as used by the down
+ * projection). saved_activations [S*k*3F] bf16, caller-owned: rows [S*k, 2F]
+ * holding a in columns [0, F) and b in [F, 2F), followed by h [S*k, F], all
+ * in slot order. Passing it to moe_scatter_ffn_bwd skips the backward's
+ * recomputation of the gate+up GEMM. out is identical to moe_scatter_ffn_fwd.
+ * workspace_bytes >= moe_scatter_ffn_workspace_bytes(); limits as the
+ * forward, and S*k*2F < 2^30.
+ */
+int moe_scatter_ffn_fwd_train(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                              const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                              int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *out,
+                              uint16_t *saved_activations, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Workspace bytes of moe_scatter_ffn_bwd: tile tables, the recomputed
  * a | b [S*k, 2F] and h [S*k, F] (bf16, slot order), slot-order copies of
  * g*dout and x [S*k, D] (bf16), fp32 input-gradient rows [S*k, D] and the
@@ -197,14 +213,18 @@ size_t moe_scatter_ffn_bwd_workspace_bytes(int32_t S, int32_t D, int32_t F, int3
  * experts with no routes get zero weight gradients; results are
  * reproducible run to run. Any output may be NULL (not all). Arguments,
  * layouts and the map as moe_scatter_ffn_fwd; topk_weights is required.
+ * saved_activations: NULL to recompute a, b and h here, or the buffer filled
+ * by moe_scatter_ffn_fwd_train for the same inputs (then no recomputation;
+ * the gradients are bit-identical); the call overwrites its a | b rows with
+ * da | db, so it serves one backward.
  * Limits: D % 64 == 0, F % 64 == 0, E <= 1024, S*D < 2^30, D*F < 2^30,
  * S*k*max(D, 2F) < 2^30 (else UNSUPPORTED).
  */
 int moe_scatter_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                         const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
-                        const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *dx,
-                        float *dw1, float *dw3, float *dw2, float *d_topk_weights, void *workspace,
-                        size_t workspace_bytes, void *stream);
+                        const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k,
+                        uint16_t *saved_activations, uint16_t *dx, float *dw1, float *dw3, float *dw2,
+                        float *d_topk_weights, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Workspace bytes of moe_parallel_linear_fwd and moe_parallel_linear_bwd for

@@ -32,8 +32,10 @@ SIGNATURES = {
     "moe_scatter_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ,
                                            _P]),
     "moe_scatter_ffn_bwd_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "moe_scatter_ffn_fwd_train": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P,
+                                                 _P, _SZ, _P]),
     "moe_scatter_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
-                                           _P, _P, _P, _SZ, _P]),
+                                           _P, _P, _P, _P, _SZ, _P]),
     "moe_parallel_linear_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_parallel_linear_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                                _SZ, _P]),
@@ -176,11 +178,13 @@ def moe_sparse_map(topk_ids: torch.Tensor, E: int, out: Optional[Tuple[torch.Ten
 def moe_scatter_ffn_fwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
                         topk_weights: torch.Tensor, expert_offsets: torch.Tensor, slot_src: torch.Tensor,
                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                        stream=None, atomic: bool = False) -> torch.Tensor:
+                        stream=None, atomic: bool = False, saved: Optional[torch.Tensor] = None) -> torch.Tensor:
     """SwiGLU experts on gathered rows + router-weighted combine -> out bf16 [S, D].
 
     atomic=False: per-route rows and an ordered combine (bitwise reproducible);
-    atomic=True: fp32 atomic scatter-add into a token accumulator (smaller workspace)."""
+    atomic=True: fp32 atomic scatter-add into a token accumulator (smaller workspace).
+    saved: a bf16 buffer of S*k*3F elements (training mode): receives a | b and h for
+    moe_scatter_ffn_bwd (see saved_activations_numel)."""
     S, D = x.shape
     E, D2, F = w1.shape
     k = topk_weights.shape[1]
@@ -194,6 +198,17 @@ def moe_scatter_ffn_fwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2:
     if out is None:
         out = torch.empty((S, D), dtype=torch.bfloat16, device=x.device)
     _dev(out, torch.bfloat16, "out", (S, D))
+    if saved is not None:
+        if atomic:
+            raise MoEError("the training-mode forward uses the per-route-rows combine")
+        _dev(saved, torch.bfloat16, "saved", (saved_activations_numel(S, F, k),))
+        need = scatter_ffn_workspace_bytes(S, D, F, E, k, False)
+        ws = _workspace(need, x.device, workspace)
+        _check(load().moe_scatter_ffn_fwd_train(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(topk_weights),
+                                                _ptr(expert_offsets), _ptr(slot_src), S, D, F, E, k, _ptr(out),
+                                                _ptr(saved), _ptr(ws), ws.numel() * ws.element_size(),
+                                                _stream(stream)), "moe_scatter_ffn_fwd_train")
+        return out
     need = scatter_ffn_workspace_bytes(S, D, F, E, k, atomic)
     ws = _workspace(need, x.device, workspace)
     # the library picks the combine from the byte count it is given
@@ -203,6 +218,11 @@ def moe_scatter_ffn_fwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2:
     return out
 
 
+def saved_activations_numel(S: int, F: int, k: int) -> int:
+    """bf16 elements of the training-mode forward's saved activations: a | b [S*k, 2F] then h [S*k, F]."""
+    return S * k * 3 * F
+
+
 def scatter_ffn_bwd_workspace_bytes(S: int, D: int, F: int, E: int, k: int) -> int:
     return int(load().moe_scatter_ffn_bwd_workspace_bytes(S, D, F, E, k))
 
@@ -210,9 +230,10 @@ def scatter_ffn_bwd_workspace_bytes(S: int, D: int, F: int, E: int, k: int) -> i
 def moe_scatter_ffn_bwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
                         topk_weights: torch.Tensor, expert_offsets: torch.Tensor, slot_src: torch.Tensor,
                         dout: torch.Tensor, need=("dx", "dw1", "dw3", "dw2", "dg"),
-                        workspace: Optional[torch.Tensor] = None, stream=None):
+                        workspace: Optional[torch.Tensor] = None, stream=None, saved: Optional[torch.Tensor] = None):
     """Backward of moe_scatter_ffn_fwd -> dict with dx bf16 [S, D], dw1 / dw3 fp32 [E, D, F],
-    dw2 fp32 [E, F, D] and dg fp32 [S, k] (the router-weight gradient), for the names in `need`."""
+    dw2 fp32 [E, F, D] and dg fp32 [S, k] (the router-weight gradient), for the names in `need`.
+    saved: the buffer of the training-mode forward (skips the recomputation; overwritten)."""
     S, D = x.shape
     E, D2, F = w1.shape
     k = topk_weights.shape[1]
@@ -224,13 +245,15 @@ def moe_scatter_ffn_bwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2:
     _dev(expert_offsets, torch.int32, "expert_offsets", (E + 1,))
     _dev(slot_src, torch.int32, "slot_src", (S * k,))
     _dev(dout, torch.bfloat16, "dout", (S, D))
+    if saved is not None:
+        _dev(saved, torch.bfloat16, "saved", (saved_activations_numel(S, F, k),))
     dev = x.device
     shapes = dict(dx=((S, D), torch.bfloat16), dw1=((E, D, F), torch.float32), dw3=((E, D, F), torch.float32),
                   dw2=((E, F, D), torch.float32), dg=((S, k), torch.float32))
     out = {n: torch.empty(shapes[n][0], dtype=shapes[n][1], device=dev) for n in need}
     ws = _workspace(scatter_ffn_bwd_workspace_bytes(S, D, F, E, k), dev, workspace)
     _check(load().moe_scatter_ffn_bwd(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(topk_weights),
-                                      _ptr(expert_offsets), _ptr(slot_src), _ptr(dout), S, D, F, E, k,
+                                      _ptr(expert_offsets), _ptr(slot_src), _ptr(dout), S, D, F, E, k, _ptr(saved),
                                       *(_ptr(out.get(n)) for n in ("dx", "dw1", "dw3", "dw2", "dg")), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)), "moe_scatter_ffn_bwd")
     return out

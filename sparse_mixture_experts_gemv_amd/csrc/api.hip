@@ -107,7 +107,33 @@ int moe_scatter_ffn_fwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
     else if (workspace_bytes >= atomic.ws_bytes) use_atomic = true;
     else return MOE_ERR_WORKSPACE_TOO_SMALL;
     return finish(smoe::launch_scatter_ffn(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, S, D, F, E, k, out,
-                                           workspace, use_atomic, reinterpret_cast<hipStream_t>(stream)));
+                                           nullptr, workspace, use_atomic, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_scatter_ffn_fwd_train(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                              const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                              int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *out,
+                              uint16_t *saved_activations, void *workspace, size_t workspace_bytes, void *stream) {
+    if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if (S == 0) return MOE_OK;
+    if (!x || !w1 || !w3 || !w2 || !topk_weights || !expert_offsets || !slot_src || !out || !workspace ||
+        !saved_activations)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (misaligned(x) || misaligned(w1) || misaligned(w3) || misaligned(w2) || misaligned(topk_weights) ||
+        misaligned(expert_offsets) || misaligned(slot_src) || misaligned(out) || misaligned(workspace) ||
+        misaligned(saved_activations))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (D % 64 != 0 || F % 64 != 0 || E > 1024) return MOE_ERR_UNSUPPORTED;
+    const int64_t N = (int64_t)S * k;
+    // as the forward, and the saved a | b rows (2F per slot) below 2 GiB
+    if (N >= ((int64_t)1 << 31) || (int64_t)S * D >= ((int64_t)1 << 30) || (int64_t)D * F >= ((int64_t)1 << 30) ||
+        N * 2 * F >= ((int64_t)1 << 30))
+        return MOE_ERR_UNSUPPORTED;
+    const smoe::FfnPlan rows = smoe::ffn_plan(S, D, F, E, k, false);
+    if (!smoe::ffn_plan_fits(rows)) return MOE_ERR_UNSUPPORTED;
+    if (workspace_bytes < rows.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return finish(smoe::launch_scatter_ffn(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, S, D, F, E, k, out,
+                                           saved_activations, workspace, false, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t moe_scatter_ffn_bwd_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k) {
@@ -117,15 +143,15 @@ size_t moe_scatter_ffn_bwd_workspace_bytes(int32_t S, int32_t D, int32_t F, int3
 
 int moe_scatter_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                         const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
-                        const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k, uint16_t *dx,
-                        float *dw1, float *dw3, float *dw2, float *d_topk_weights, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+                        const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k,
+                        uint16_t *saved_activations, uint16_t *dx, float *dw1, float *dw3, float *dw2,
+                        float *d_topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
     if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
     if (!dx && !dw1 && !dw3 && !dw2 && !d_topk_weights) return MOE_ERR_INVALID_ARGUMENT;
     if (!w1 || !w3 || !w2 || !expert_offsets || !workspace) return MOE_ERR_INVALID_ARGUMENT;
     if (S > 0 && (!x || !topk_weights || !slot_src || !dout)) return MOE_ERR_INVALID_ARGUMENT;
     const void *ptrs[] = {x, w1, w3, w2, topk_weights, expert_offsets, slot_src, dout, dx, dw1, dw3, dw2,
-                          d_topk_weights, workspace};
+                          d_topk_weights, workspace, saved_activations};
     for (const void *q : ptrs)
         if (q && misaligned(q)) return MOE_ERR_INVALID_ARGUMENT;
     if (D % 64 != 0 || F % 64 != 0 || E > 1024) return MOE_ERR_UNSUPPORTED;
@@ -139,7 +165,7 @@ int moe_scatter_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
     if (workspace_bytes < pl.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (S == 0 && !dw1 && !dw3 && !dw2) return MOE_OK;  // with a weight gradient requested, zeros are written
     return finish(smoe::launch_ffn_bwd(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, dout, S, D, F, E, k,
-                                       dx, dw1, dw3, dw2, d_topk_weights, workspace,
+                                       saved_activations, dx, dw1, dw3, dw2, d_topk_weights, workspace,
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 

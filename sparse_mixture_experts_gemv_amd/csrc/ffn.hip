@@ -257,9 +257,9 @@ static void launch_pp_streamk(const GemmParams &p0, hipStream_t stream) {
 // skip the MFMAs and row loads of missing rows.
 template <int MODE>
 static void launch_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t stream) {
-    const int kid = MODE == kGateUp ? kKGateUp : kKDown;
+    const int kid = (MODE == kGateUp || MODE == kGateUpSave) ? kKGateUp : kKDown;
     prof_begin(stream, kid);
-    if constexpr (MODE == kGateUp) {
+    if constexpr (MODE == kGateUp || MODE == kGateUpSave) {
         switch (bm) {
             case 256: launch_pp_persistent<256, 128, MODE, 64, 2>(p, stream); break;
             case 192: launch_pp_persistent<192, 128, MODE, 64, 3, 2, true>(p, stream); break;
@@ -289,8 +289,8 @@ static void launch_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t st
 
 hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                               const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
-                              int S, int D, int F, int E, int k, uint16_t *out, void *workspace, bool atomic,
-                              hipStream_t stream) {
+                              int S, int D, int F, int E, int k, uint16_t *out, uint16_t *saved, void *workspace,
+                              bool atomic, hipStream_t stream) {
     const FfnPlan pl = ffn_plan(S, D, F, E, k, atomic);
     char *ws = reinterpret_cast<char *>(workspace);
     int4 *tiles_up = reinterpret_cast<int4 *>(ws + pl.tiles_up_off);
@@ -336,19 +336,24 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.A = x;
     p.B0 = w1;
     p.B1 = w3;
-    p.C = h;
+    // training mode: a | b and h go to the caller's buffer for the backward
+    uint16_t *h_rows = saved ? saved + (size_t)N * 2 * F : h;
+    p.C = saved ? static_cast<void *>(saved) : static_cast<void *>(h);
+    p.C2 = h_rows;
     p.M = N;
     p.N = F;
     p.K = D;
     p.valid_mtiles = valid_counts;
-    launch_gemm<kGateUp>(pl.bm_up, (int64_t)N / E, p, stream);
+    if (saved) launch_gemm<kGateUpSave>(pl.bm_up, (int64_t)N / E, p, stream);
+    else launch_gemm<kGateUp>(pl.bm_up, (int64_t)N / E, p, stream);
 
     // down + scatter-add (atomic) or per-route rows: A = h (slot order), K = F, N = D
     p.tiles = tiles_down;
     p.order = order_down;
     p.valid_mtiles = valid_counts + 1;
     p.n_mtiles = pl.n_mtiles_down;
-    p.A = h;
+    p.A = h_rows;
+    p.C2 = nullptr;
     p.B0 = w2;
     p.B1 = nullptr;
     p.C = acc;

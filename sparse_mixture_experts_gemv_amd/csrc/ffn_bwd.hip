@@ -12,7 +12,8 @@
 //
 // Kernels (one stream, no host synchronisation):
 //   tile tables     the expert tiles and block orders of the four GEMMs
-//   recompute       gate+up GEMM saving a, b (bf16, [S*k, 2F]) and h
+//   recompute       gate+up GEMM saving a, b (bf16, [S*k, 2F]) and h (skipped
+//                   when the training-mode forward kept them)
 //   slot rows       g dout[t] and x[t] copied to slot order (weight GEMMs)
 //   dh              W2^T GEMM of the gathered dout rows; its epilogue turns
 //                   a, b into da, db in place and writes <h, c> partials
@@ -160,8 +161,8 @@ static void launch_bwd_bt(int bm, int64_t avg, const GemmParams &p, hipStream_t 
 
 hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                           const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
-                          const uint16_t *dout, int S, int D, int F, int E, int k, uint16_t *dx, float *dw1,
-                          float *dw3, float *dw2, float *dg, void *workspace, hipStream_t stream) {
+                          const uint16_t *dout, int S, int D, int F, int E, int k, uint16_t *saved, uint16_t *dx,
+                          float *dw1, float *dw3, float *dw2, float *dg, void *workspace, hipStream_t stream) {
     const FfnBwdPlan pl = ffn_bwd_plan(S, D, F, E, k);
     char *ws = reinterpret_cast<char *>(workspace);
     const int N = S * k;
@@ -169,8 +170,9 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
     int4 *tiles_r = reinterpret_cast<int4 *>(ws + pl.tiles_r);
     int4 *tiles_b = reinterpret_cast<int4 *>(ws + pl.tiles_b);
     int4 *tiles_x = reinterpret_cast<int4 *>(ws + pl.tiles_x);
-    uint16_t *ab = reinterpret_cast<uint16_t *>(ws + pl.ab);
-    uint16_t *h = reinterpret_cast<uint16_t *>(ws + pl.h);
+    // a | b and h: saved by the training-mode forward, else recomputed here
+    uint16_t *ab = saved ? saved : reinterpret_cast<uint16_t *>(ws + pl.ab);
+    uint16_t *h = saved ? saved + (size_t)N * 2 * F : reinterpret_cast<uint16_t *>(ws + pl.h);
     uint16_t *dyg = reinterpret_cast<uint16_t *>(ws + pl.dyg);
     uint16_t *xg = reinterpret_cast<uint16_t *>(ws + pl.xg);
     float *rows = reinterpret_cast<float *>(ws + pl.rows);
@@ -219,9 +221,11 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
     p.C2 = h;
     p.N = F;
     p.K = D;
-    prof_begin(stream, kKBwdRecompute);
-    launch_recompute(pl.bm_r, p, stream);
-    prof_end(stream, kKBwdRecompute);
+    if (!saved) {
+        prof_begin(stream, kKBwdRecompute);
+        launch_recompute(pl.bm_r, p, stream);
+        prof_end(stream, kKBwdRecompute);
+    }
 
     // c = dout[t] W2[e]^T; epilogue: da, db over a, b and the <h, c> partials
     p.tiles = tiles_b;

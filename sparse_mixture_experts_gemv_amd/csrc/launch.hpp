@@ -64,8 +64,8 @@ int device_cus();
 
 hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                               const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
-                              int S, int D, int F, int E, int k, uint16_t *out, void *workspace, bool atomic,
-                              hipStream_t stream);
+                              int S, int D, int F, int E, int k, uint16_t *out, uint16_t *saved, void *workspace,
+                              bool atomic, hipStream_t stream);
 
 // ---- ParallelLinear ----
 struct PlPlan {
@@ -102,8 +102,8 @@ inline bool ffn_bwd_plan_fits(const FfnBwdPlan &pl) {
 }
 hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                           const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
-                          const uint16_t *dout, int S, int D, int F, int E, int k, uint16_t *dx, float *dw1,
-                          float *dw3, float *dw2, float *dg, void *workspace, hipStream_t stream);
+                          const uint16_t *dout, int S, int D, int F, int E, int k, uint16_t *saved, uint16_t *dx,
+                          float *dw1, float *dw3, float *dw2, float *dg, void *workspace, hipStream_t stream);
 
 // ---- router ----
 size_t route_ws_bytes(int64_t S, int64_t E);

@@ -28,7 +28,7 @@ def header_functions():
 def test_exports_every_declared_symbol(lib):
     import sparse_mixture_experts_gemv_amd._lib as b
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.SIGNATURES)
@@ -120,8 +120,8 @@ def test_parallel_linear_validation(lib):
 
 def test_ffn_bwd_validation(lib):
     b = lib.moe_scatter_ffn_bwd
-    args = lambda S=16, D=64, F=128, E=8, k=2, ws=1 << 30, dx=FAKE, dg=FAKE, x=FAKE, tw=FAKE: (
-        x, FAKE, FAKE, FAKE, tw, FAKE, FAKE, FAKE, S, D, F, E, k, dx, FAKE, FAKE, FAKE, dg, FAKE, ws, None)
+    args = lambda S=16, D=64, F=128, E=8, k=2, ws=1 << 30, dx=FAKE, dg=FAKE, x=FAKE, tw=FAKE, sv=None: (
+        x, FAKE, FAKE, FAKE, tw, FAKE, FAKE, FAKE, S, D, F, E, k, sv, dx, FAKE, FAKE, FAKE, dg, FAKE, ws, None)
     assert b(*args(k=9)) == 1
     assert b(*args(x=None)) == 1
     assert b(*args(tw=None)) == 1                 # the router weights are required
@@ -130,6 +130,14 @@ def test_ffn_bwd_validation(lib):
     assert b(*args(F=80)) == 2
     assert b(*args(E=2048)) == 2
     assert b(*args(ws=4096)) == 3
+    assert b(*args(sv=MISALIGNED)) == 1
+    t = lib.moe_scatter_ffn_fwd_train
+    targs = lambda S=16, D=64, F=128, E=8, k=2, ws=1 << 30, sv=FAKE: (
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, S, D, F, E, k, FAKE, sv, FAKE, ws, None)
+    assert t(*targs(sv=None)) == 1               # the saved-activations buffer is required
+    assert t(*targs(F=80)) == 2
+    assert t(*targs(ws=4096)) == 3
+    assert t(*targs(S=0, sv=None)) == 0
     n = lib.moe_scatter_ffn_bwd_workspace_bytes(4096, 4096, 14336, 8, 2)
     N = 8192
     base = N * 2 * 14336 * 2 + N * 14336 * 2 + 2 * N * 4096 * 2 + N * 4096 * 4

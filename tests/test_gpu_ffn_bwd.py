@@ -170,3 +170,36 @@ def test_ffn_bwd_full_size_sampled(oracle_lib, name, ntok):
         grad_close(got["dw1"][e, :, c0:c0 + 64].cpu().numpy(), r["dw1"][le], f"{name} dw1[{e}] cols {c0}+64")
         grad_close(got["dw3"][e, :, c0:c0 + 64].cpu().numpy(), r["dw3"][le], f"{name} dw3[{e}] cols {c0}+64")
         grad_close(got["dw2"][e, c0:c0 + 64, :].cpu().numpy(), r["dw2"][le], f"{name} dw2[{e}] rows {c0}+64")
+
+
+@pytest.mark.parametrize("S,D,F,E,k", [(1000, 128, 192, 4, 2), (600, 128, 192, 8, 2), (200, 128, 256, 16, 2)])
+def test_ffn_training_forward_and_saved_backward(S, D, F, E, k):
+    """The training-mode forward returns the same output bit for bit and keeps a, b and h (a and b
+    checked against an fp64 product); a backward fed those saved activations skips the
+    recomputation and gives bit-identical gradients."""
+    import sparse_mixture_experts_gemv_amd as smoe
+    p, ids, w, dout = problem(S, D, F, E, k, None, seed=S + 3 * E)
+    ids_d, w_d = torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+    _, offsets, _, src = smoe.moe_sparse_map(ids_d, E)
+    out = smoe.moe_scatter_ffn_fwd(p["x"], p["w1"], p["w3"], p["w2"], w_d, offsets, src)
+    saved = torch.empty(smoe.saved_activations_numel(S, F, k), dtype=torch.bfloat16, device=DEV)
+    out_t = smoe.moe_scatter_ffn_fwd(p["x"], p["w1"], p["w3"], p["w2"], w_d, offsets, src, saved=saved)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_t)
+    N = S * k
+    ab = saved[:N * 2 * F].view(N, 2 * F).double().cpu()
+    srcs = src.cpu().numpy()
+    tok = torch.from_numpy(srcs // k)
+    exp = torch.from_numpy(ids.reshape(-1)[srcs].astype(np.int64))
+    x64 = p["x"].double().cpu()[tok]
+    a_ref = torch.einsum("nd,ndf->nf", x64, p["w1"].double().cpu()[exp])
+    b_ref = torch.einsum("nd,ndf->nf", x64, p["w3"].double().cpu()[exp])
+    for got, ref, name in ((ab[:, :F], a_ref, "a"), (ab[:, F:], b_ref, "b")):
+        rel = float((got - ref).abs().max() / ref.abs().max())
+        say(f"  saved {name}: max-rel {rel:.3e}")
+        assert rel < 1e-2, (name, rel)
+    recompute = smoe.moe_scatter_ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], w_d, offsets, src, dout)
+    from_saved = smoe.moe_scatter_ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], w_d, offsets, src, dout, saved=saved)
+    torch.cuda.synchronize()
+    for n in recompute:
+        assert torch.equal(recompute[n], from_saved[n]), n
