@@ -379,6 +379,38 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
     // ---- epilogue (C layout: lane holds column lane % 16, rows 4 (lane / 16) + r) ----
     const int col_in_tile = lane & 15;
     const int row_grp = (lane >> 4) * 4;
+    if constexpr (MODE == kGateUp) {
+        // h is staged through LDS (the operand ring is free once every wave is
+        // past the loop) and leaves in 16-byte stores of whole tile rows
+        // instead of 2-byte stores that touch 32-byte pieces of four rows.
+        constexpr int HS = BN + 8;  // bf16 per staged row (16-byte pad)
+        static_assert(BM * HS * 2 <= PPGeom<BM, BN, MODE, BK, STAGES, STAGES_A>::SMEM, "h tile fits the ring");
+        uint16_t *sh = reinterpret_cast<uint16_t *>(smem);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const float g = acc[0][i][j][r], u = acc[1][i][j][r];
+                    const float sg = g / (1.0f + __expf(-g));
+                    sh[((WM * i + wm) * 16 + row_grp + r) * HS + wn * WTN + j * 16 + col_in_tile] =
+                        f32_to_bf16_bits(sg * u);
+                }
+        __syncthreads();
+        constexpr int TPR = BN / 8;  // threads per row, 8 bf16 each
+        uint16_t *h = reinterpret_cast<uint16_t *>(p.C);
+        const int c = (tid % TPR) * 8;
+        for (int rb = tid / TPR; rb < BM; rb += 512 / TPR) {
+            const int slot = row0 + rb;
+            if (slot < row1 && n0 + c < N)
+                *reinterpret_cast<uint4 *>(h + (size_t)slot * N + n0 + c) =
+                    *reinterpret_cast<const uint4 *>(sh + rb * HS + c);
+        }
+        __syncthreads();  // the next tile's DMA may overwrite the staging area
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
