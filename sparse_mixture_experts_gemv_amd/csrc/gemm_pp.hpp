@@ -411,6 +411,50 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
         __syncthreads();  // the next tile's DMA may overwrite the staging area
         return;
     }
+    if constexpr (MODE == kDownRows) {
+        // the fp32 rows are staged through LDS in passes of whole 32-row
+        // groups and leave as 16-byte stores of whole tile rows (BN floats of
+        // route row f) instead of 4-byte stores that touch 64-byte pieces of
+        // four rows; the route's gate is applied on the way out
+        constexpr int YS = BN + 4;  // floats per staged row
+        constexpr int SMEM = PPGeom<BM, BN, MODE, BK, STAGES, STAGES_A>::SMEM;
+        constexpr int PASSES = (BM * YS * 4 <= SMEM) ? 1 : (MT % 2 == 0 && BM / 2 * YS * 4 <= SMEM) ? 2 : MT;
+        static_assert(MT % PASSES == 0 && BM / PASSES * YS * 4 <= SMEM, "staged rows fit the ring");
+        constexpr int MTP = MT / PASSES;  // 16-row blocks per wave and pass
+        constexpr int RP = BM / PASSES;   // tile rows per pass
+        constexpr int TPR = BN / 4;       // threads per row, 4 floats each
+        float *sy = reinterpret_cast<float *>(smem);
+        float *y = reinterpret_cast<float *>(p.C);
+        const int c = (tid % TPR) * 4;
+        __syncthreads();
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+#pragma unroll
+            for (int il = 0; il < MTP; ++il)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        sy[((WM * il + wm) * 16 + row_grp + r) * YS + wn * WTN + j * 16 + col_in_tile] =
+                            acc[0][ps * MTP + il][j][r];
+            __syncthreads();
+            for (int rl = tid / TPR; rl < RP; rl += 512 / TPR) {
+                const int slot = row0 + ps * RP + rl;
+                if (slot < row1 && n0 + c < N) {
+                    const int f = p.slot_src[slot];
+                    const float w = p.gate ? p.gate[f] : 1.0f;
+                    float4 v = *reinterpret_cast<const float4 *>(sy + rl * YS + c);
+                    v.x *= w;
+                    v.y *= w;
+                    v.z *= w;
+                    v.w *= w;
+                    *reinterpret_cast<float4 *>(y + (size_t)f * N + n0 + c) = v;
+                }
+            }
+            __syncthreads();  // before the next pass or the next tile's DMA reuses the area
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
