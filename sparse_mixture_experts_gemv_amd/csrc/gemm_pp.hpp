@@ -379,34 +379,63 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
     // ---- epilogue (C layout: lane holds column lane % 16, rows 4 (lane / 16) + r) ----
     const int col_in_tile = lane & 15;
     const int row_grp = (lane >> 4) * 4;
-    if constexpr (MODE == kGateUp) {
-        // h is staged through LDS (the operand ring is free once every wave is
-        // past the loop) and leaves in 16-byte stores of whole tile rows
-        // instead of 2-byte stores that touch 32-byte pieces of four rows.
+    if constexpr (MODE == kGateUp || MODE == kGateUpSave || MODE == kLinBf16) {
+        // bf16 outputs are staged through LDS (the operand ring is free once
+        // every wave is past the loop) and leave in 16-byte stores of whole
+        // tile rows instead of 2-byte stores that touch 32-byte pieces of four
+        // rows: h (kGateUp), a, b and h (kGateUpSave, one after the other),
+        // or the gated product (kLinBf16, the gate applied while staging).
         constexpr int HS = BN + 8;  // bf16 per staged row (16-byte pad)
-        static_assert(BM * HS * 2 <= PPGeom<BM, BN, MODE, BK, STAGES, STAGES_A>::SMEM, "h tile fits the ring");
+        static_assert(BM * HS * 2 <= PPGeom<BM, BN, MODE, BK, STAGES, STAGES_A>::SMEM, "tile fits the ring");
+        constexpr int NOUT = (MODE == kGateUpSave) ? 3 : 1;
         uint16_t *sh = reinterpret_cast<uint16_t *>(smem);
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const float g = acc[0][i][j][r], u = acc[1][i][j][r];
-                    const float sg = g / (1.0f + __expf(-g));
-                    sh[((WM * i + wm) * 16 + row_grp + r) * HS + wn * WTN + j * 16 + col_in_tile] =
-                        f32_to_bf16_bits(sg * u);
-                }
-        __syncthreads();
         constexpr int TPR = BN / 8;  // threads per row, 8 bf16 each
-        uint16_t *h = reinterpret_cast<uint16_t *>(p.C);
         const int c = (tid % TPR) * 8;
-        for (int rb = tid / TPR; rb < BM; rb += 512 / TPR) {
-            const int slot = row0 + rb;
-            if (slot < row1 && n0 + c < N)
-                *reinterpret_cast<uint4 *>(h + (size_t)slot * N + n0 + c) =
-                    *reinterpret_cast<const uint4 *>(sh + rb * HS + c);
+#pragma unroll
+        for (int q = 0; q < NOUT; ++q) {
+            __syncthreads();  // the loop's reads, or the previous output's stores, are done
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = (WM * i + wm) * 16 + row_grp + r;
+                    float w = 1.0f;
+                    if constexpr (MODE == kLinBf16) {
+                        const int slot = min(row0 + row, row1 - 1);
+                        w = p.gate ? p.gate[p.slot_src[slot]] : 1.0f;
+                    }
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        float v;
+                        if constexpr (MODE == kLinBf16) {
+                            v = w * acc[0][i][j][r];
+                        } else {
+                            const float g = acc[0][i][j][r], u = acc[1][i][j][r];
+                            if (q == 0 && MODE == kGateUpSave) v = g;
+                            else if (q == 1) v = u;
+                            else v = (g / (1.0f + __expf(-g))) * u;  // SiLU(a) * b, as stored in h
+                        }
+                        sh[row * HS + wn * WTN + j * 16 + col_in_tile] = f32_to_bf16_bits(v);
+                    }
+                }
+            __syncthreads();
+            // destination: h / y rows [rows, N] (kGateUp, kLinBf16, q = 2 of kGateUpSave: C2),
+            // a | b rows [rows, 2N] (kGateUpSave q = 0, 1: C)
+            uint16_t *dst;
+            size_t ld;
+            if (MODE == kGateUpSave && q < 2) {
+                dst = reinterpret_cast<uint16_t *>(p.C) + (size_t)q * N;
+                ld = 2 * (size_t)N;
+            } else {
+                dst = reinterpret_cast<uint16_t *>(MODE == kGateUpSave ? p.C2 : p.C);
+                ld = N;
+            }
+            for (int rb = tid / TPR; rb < BM; rb += 512 / TPR) {
+                const int slot = row0 + rb;
+                if (slot < row1 && n0 + c < N)
+                    *reinterpret_cast<uint4 *>(dst + (size_t)slot * ld + n0 + c) =
+                        *reinterpret_cast<const uint4 *>(sh + rb * HS + c);
+            }
         }
         __syncthreads();  // the next tile's DMA may overwrite the staging area
         return;
