@@ -395,6 +395,7 @@ def main():
     ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "train", "pl_fwd", "pl_bwd", "map_sweep"],
                     help="layer: the MoE forward (default); ffn_bwd: the expert FFN backward; "
                          "pl_fwd / pl_bwd: ParallelLinear up-projection")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run three device-to-device copies of BYTES (HBM counter calibration)")
     args = ap.parse_args()
@@ -462,6 +463,20 @@ def main():
     kern = smoe.profile_stop()
     ms = t0.elapsed_time(t1) / args.steps
 
+    graph_ms = None
+    if not args.no_graph:
+        # the same forward captured once as a HIP graph and replayed: no per-kernel launch cost
+        layer.capture(p["x"], topk)
+        for _ in range(args.warmup):
+            layer.replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            layer.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = t0.elapsed_time(t1) / args.steps
+
     flops = layer_flops(S, D, F, E, k, with_router=topk is None)
     tokens_per_s = S / (ms / 1e3)
     kernels = {name: {"avg_us": 1e3 * tot / n, "launches": n} for name, (tot, n) in kern.items()}
@@ -493,6 +508,8 @@ def main():
         "kernels": {n: {"avg_us": round(v["avg_us"], 2), "launches": v["launches"]} for n, v in kernels.items()},
         "wall_s_timed_region": round(wall, 3),
     }
+    if graph_ms is not None:
+        rec["graph_replay"] = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(S / (graph_ms / 1e3), 1)}
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 CPU oracle on a sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, p, args.cpu_seconds)

@@ -343,6 +343,27 @@ class MoELayer:
                      scatter_ffn_workspace_bytes(S, D, F, E, k, atomic))
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
+    def capture(self, x: torch.Tensor, topk: Optional[Tuple[torch.Tensor, torch.Tensor]] = None) -> None:
+        """Record forward(x, topk) as a HIP graph (torch.cuda.CUDAGraph); replay() reruns it on the same
+        buffers, so refill x (and topk) in place between replays. The path issues kernels only (no memsets,
+        no host synchronisation), so it captures whole; replays skip the per-kernel launch cost."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.forward(x, topk)  # warm-up outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x, topk)
+        self.graph = graph
+
+    def replay(self) -> torch.Tensor:
+        """Rerun the captured forward on the current stream; returns the output buffer."""
+        if getattr(self, "graph", None) is None:
+            raise MoEError("capture() first")
+        self.graph.replay()
+        return self.out
+
     def forward(self, x: torch.Tensor, topk: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, stream=None):
         if topk is None:
             moe_route_topk(x, self.w_gate, self.k, self.ids, self.weights, self.ws, stream)
