@@ -261,7 +261,7 @@ static void launch_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t st
     prof_begin(stream, kid);
     if constexpr (MODE == kGateUp || MODE == kGateUpSave) {
         switch (bm) {
-            case 256: launch_pp_persistent<256, 128, MODE, 64, 2>(p, stream); break;
+            case 256: launch_pp_persistent<256, 128, MODE, 64, 2, 2, true>(p, stream); break;
             case 192: launch_pp_persistent<192, 128, MODE, 64, 3, 2, true>(p, stream); break;
             case 64: launch_pp_persistent<64, 128, MODE, 64, 3>(p, stream); break;
             default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;

@@ -69,16 +69,27 @@ def test_ffn_skewed_single_expert(oracle_lib, atomic):
     assert_close(got, ref, f"two hot experts {'atomic' if atomic else 'rows'}", configured=False)
 
 
+ROW_EDGES = {
+    # mean 120 rows per expert -> 192-row tiles: 8-row load groups (7, 8, 9),
+    # 16-row MFMA blocks (15, 16, 17), wave row groups (31, 33, 96, 128, 160),
+    # a full tile (192), one row past it (193) and a many-tile expert
+    "192": (960, 2, [1, 7, 8, 9, 15, 16, 17, 31, 33, 96, 128, 160, 191, 192, 193]),
+    # mean 225 rows per expert -> 256-row gate+up tiles (128-row down tiles):
+    # the same edges around 256, 512 and a tail expert
+    "256": (1800, 2, [1, 9, 16, 17, 33, 128, 160, 255, 256, 257, 300, 400, 512, 513, 600]),
+}
+
+
 @pytest.mark.parametrize("atomic", [False, True], ids=["rows", "atomic"])
-def test_ffn_short_tiles_row_edges(oracle_lib, atomic):
-    """Experts whose row counts straddle every edge of the short-tile path of
-    the 192-row tiles (mean 120 rows per expert): 8-row load groups (7, 8,
-    9), 16-row MFMA blocks (15, 16, 17), wave row groups (31, 33, 96, 128,
-    160), a full tile (192), one row past it (193) and a many-tile expert."""
-    S, k, E = 960, 2, 16
-    counts = [1, 7, 8, 9, 15, 16, 17, 31, 33, 96, 128, 160, 191, 192, 193]
+@pytest.mark.parametrize("family", sorted(ROW_EDGES))
+def test_ffn_short_tiles_row_edges(oracle_lib, family, atomic):
+    """Experts whose row counts straddle every edge of the short-tile path
+    (tiles of an expert's last rows skip the MFMAs and loads of missing rows)."""
+    S, k, counts = ROW_EDGES[family]
+    counts = list(counts)
     counts.append(S * k - sum(counts))
-    assert max(counts) <= S
+    E = len(counts)
+    assert max(counts) <= S and min(counts) >= 0
     flat = np.repeat(np.arange(E, dtype=np.int32), counts)   # sorted by expert
     ids = np.stack([flat[:S], flat[S:]], axis=1)             # distinct per token since every count <= S
     assert np.all(ids[:, 0] != ids[:, 1])
@@ -87,7 +98,7 @@ def test_ffn_short_tiles_row_edges(oracle_lib, atomic):
     w = np.random.default_rng(1).dirichlet(np.ones(k), size=S).astype(np.float32)
     got = gpu_ffn(p, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), atomic)
     ref = oracle_ffn_rows(oracle_lib, p, ids, w, np.arange(S))
-    assert_close(got, ref, f"short-tile row edges {'atomic' if atomic else 'rows'}", configured=False)
+    assert_close(got, ref, f"short-tile row edges ({family}) {'atomic' if atomic else 'rows'}", configured=False)
 
 
 def test_ffn_rows_combine_is_bitwise_reproducible():
