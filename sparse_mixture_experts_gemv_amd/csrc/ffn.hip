@@ -150,7 +150,9 @@ void launch_tile_table(const int32_t *offsets, int E, int N, const TileTableArgs
 void launch_combine_rows(const float *y, uint16_t *out, int S, int D, int k, hipStream_t stream) {
     const size_t n4 = (size_t)S * D / 4;
     prof_begin(stream, kKCombine);
-    combine_rows_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(y),
+    // one float4 per thread where the grid allows it: with few tokens the
+    // k loads of a thread are its whole latency chain
+    combine_rows_kernel<<<grid_for(n4, 256), 256, 0, stream>>>(reinterpret_cast<const float4 *>(y),
                                                                     reinterpret_cast<uint2 *>(out), S, D / 4, k);
     prof_end(stream, kKCombine);
 }

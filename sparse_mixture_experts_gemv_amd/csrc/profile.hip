@@ -39,7 +39,8 @@ const char *kNames[kNumKernelIds] = {"route_logits_gemm", "route_topk_softmax", 
                                      "ffn_gate_up_gemm",  "ffn_down_scatter_gemm", "ffn_finalize",
                                      "ffn_combine",       "pl_gemm",            "pl_dx_gemm", "pl_wgrad_gemm",
                                      "pl_prep",           "pl_finalize",        "bwd_recompute_gemm",
-                                     "bwd_dh_gemm",       "bwd_prep",           "bwd_wgrad_gemm", "bwd_dx_gemm"};
+                                     "bwd_dh_gemm",       "bwd_prep",           "bwd_wgrad_gemm", "bwd_dx_gemm",
+                                     "smap_small"};
 
 }  // namespace
 

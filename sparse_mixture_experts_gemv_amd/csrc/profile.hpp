@@ -30,6 +30,7 @@ enum KernelId {
     kKBwdPrep,
     kKBwdWgrad,
     kKBwdDx,
+    kKMapSmall,
     kNumKernelIds
 };
 

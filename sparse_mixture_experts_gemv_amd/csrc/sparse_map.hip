@@ -195,6 +195,107 @@ __global__ __launch_bounds__(256) void smap_assign_kernel(const int32_t *__restr
     }
 }
 
+// The whole map in one workgroup of 1024 threads, for maps of at most
+// kSmallMapRoutes routes (decode-sized batches), where the three launches
+// of the general path cost more than the work. Wave w takes the contiguous
+// chunk [w L, (w + 1) L) of routes, so a route's rank among the routes of its
+// expert is: earlier waves' counts of that expert, then earlier groups of 64
+// in its own wave, then lower lanes of its own group -- the same stable slot
+// as the general path.
+constexpr int kSmallMapRoutes = 8192;
+constexpr int kSmallMapWaves = 16;
+
+__global__ __launch_bounds__(1024) void smap_small_kernel(const int32_t *__restrict__ ids, int N, int E, int nbits,
+                                                          int L, int32_t *__restrict__ expert_counts,
+                                                          int32_t *__restrict__ expert_offsets,
+                                                          int32_t *__restrict__ sparse_rows,
+                                                          int32_t *__restrict__ slot_src) {
+    __shared__ int32_t s_cnt[kSmallMapWaves * kMaxExperts];  // [wave][expert]: count, then base
+    __shared__ int s_tmp[kSmallMapWaves];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int32_t *my = s_cnt + w * E;
+    for (int e = lane; e < E; e += 64) my[e] = 0;
+    const int base = w * L;
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // pass 1: per-wave counts (only a group's lowest lane of an expert writes)
+    for (int g0 = 0; g0 < L; g0 += 64 * kMapUnroll) {
+        int ev[kMapUnroll];
+#pragma unroll
+        for (int u = 0; u < kMapUnroll; ++u) {
+            const int f = base + g0 + 64 * u + lane;
+            ev[u] = f < N ? ids[f] : E;
+        }
+#pragma unroll
+        for (int u = 0; u < kMapUnroll; ++u) {
+            int e = ev[u];
+            if ((unsigned)e >= (unsigned)E) e = E;
+            const unsigned long long m = match_any(e, nbits);
+            const int leader = __ffsll(m) - 1;
+            if (lane == leader && e < E) my[e] += __popcll(m);
+        }
+    }
+    __syncthreads();
+    // totals and their exclusive scan (thread e owns expert e; E <= 1024), then
+    // each wave's starting slot per expert, in wave order
+    const int e = threadIdx.x;
+    int tot_e = 0;
+    if (e < E)
+        for (int i = 0; i < kSmallMapWaves; ++i) tot_e += s_cnt[i * E + e];
+    int x = tot_e;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    int off = x - tot_e, total = 0;
+#pragma unroll
+    for (int i = 0; i < kSmallMapWaves; ++i) {
+        if (i < w) off += s_tmp[i];
+        total += s_tmp[i];
+    }
+    if (e < E) {
+        expert_counts[e] = tot_e;
+        expert_offsets[e] = off;
+        int run = off;
+        for (int i = 0; i < kSmallMapWaves; ++i) {
+            const int c = s_cnt[i * E + e];
+            s_cnt[i * E + e] = run;
+            run += c;
+        }
+    }
+    if (e == 0) expert_offsets[E] = total;
+    __syncthreads();
+    // pass 2: slots
+    for (int g0 = 0; g0 < L; g0 += 64 * kMapUnroll) {
+        int ev[kMapUnroll];
+#pragma unroll
+        for (int u = 0; u < kMapUnroll; ++u) {
+            const int f = base + g0 + 64 * u + lane;
+            ev[u] = f < N ? ids[f] : E;
+        }
+#pragma unroll
+        for (int u = 0; u < kMapUnroll; ++u) {
+            const int f = base + g0 + 64 * u + lane;
+            int ex = ev[u];
+            if ((unsigned)ex >= (unsigned)E) ex = E;
+            const unsigned long long m = match_any(ex, nbits);
+            const int leader = __ffsll(m) - 1;
+            int b = (lane == leader && ex < E) ? my[ex] : 0;
+            b = __shfl(b, leader);
+            if (ex < E) {
+                const int slot = b + __popcll(m & lt);
+                sparse_rows[f] = slot;
+                slot_src[slot] = f;
+            } else if (f < N) {
+                sparse_rows[f] = -1;
+            }
+            if (lane == leader && ex < E) my[ex] = b + __popcll(m);
+        }
+    }
+}
+
 __global__ void smap_empty_kernel(int E, int32_t *expert_counts, int32_t *expert_offsets) {
     for (int e = threadIdx.x; e <= E; e += blockDim.x) {
         if (e < E) expert_counts[e] = 0;
@@ -227,6 +328,16 @@ hipError_t launch_sparse_map(const int32_t *ids, int N, int E, int32_t *expert_c
         return hipGetLastError();
     }
     const SparseMapPlan pl = sparse_map_plan(N, E);
+    if (N <= kSmallMapRoutes) {
+        // chunks of whole 64 * kMapUnroll groups, one per wave
+        constexpr int G = 64 * kMapUnroll;
+        const int L = ((N + kSmallMapWaves - 1) / kSmallMapWaves + G - 1) / G * G;
+        prof_begin(stream, kKMapSmall);
+        smap_small_kernel<<<1, 1024, 0, stream>>>(ids, N, E, pl.nbits, L, expert_counts, expert_offsets, sparse_rows,
+                                                  slot_src);
+        prof_end(stream, kKMapSmall);
+        return hipGetLastError();
+    }
     int32_t *cnt = reinterpret_cast<int32_t *>(workspace);
     int32_t *totals = cnt + (size_t)E * pl.nsub;
     const int blocks = (pl.nsub + kMapWaves - 1) / kMapWaves;
