@@ -594,9 +594,11 @@ __device__ __forceinline__ bool pp_full_tile(const GemmParams &p, int mt) {
 // while the same workgroup already streams its next tile.
 //
 // With SKIP_ROWS, tiles holding fewer than BM rows run pp_tile's PARTIAL form
-// (a second copy of the main loop). Measured, that pays where most tiles are
-// short (a 192-row tile over experts of ~100-160 rows: -5 to -7 %), and costs
-// ~3 % where nearly all tiles are full, so only those launches enable it.
+// (a second copy of the main loop). Measured, that pays where many tiles are
+// short (a 192-row tile over experts of ~100-160 rows: -5 to -7 %; 256-row
+// tiles over experts of ~210-300 rows: -4 %) and is neutral on the 256-row
+// gate+up tile where nearly all tiles are full; other launches over mostly
+// full tiles leave it off (the second loop copy has cost up to ~3 % there).
 template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool SKIP_ROWS = false, int FLAGS = 0>
 __global__ __launch_bounds__(512) void grouped_gemm_pp_persistent_kernel(const GemmParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[PPGeom<BM, BN, MODE, BK, STAGES, STAGES_A>::SMEM];

@@ -101,9 +101,11 @@ def test_ffn_short_tiles_row_edges(oracle_lib, family, atomic):
     assert_close(got, ref, f"short-tile row edges ({family}) {'atomic' if atomic else 'rows'}", configured=False)
 
 
-def test_ffn_rows_combine_is_bitwise_reproducible():
-    """The ordered combine gives the same bits on every call, also for k = 8."""
-    cfg = wl.MoEConfig("repro", 62, 500, 256, 192, 64, 8, None)
+@pytest.mark.parametrize("S", [500, 40])
+def test_ffn_rows_combine_is_bitwise_reproducible(S):
+    """The ordered combine gives the same bits on every call, also for k = 8
+    and for decode-sized batches (S = 40: 5 rows per expert, 32-row tiles)."""
+    cfg = wl.MoEConfig("repro", 62, S, 256, 192, 64, 8, None)
     p = make_problem(cfg)
     ids, w = routing_for(p, seed=5)
     a = gpu_ffn(p, ids, w)

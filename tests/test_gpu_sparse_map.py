@@ -1,6 +1,7 @@
 """moe_sparse_map on the GPU: bit-exact against the oracle's stable counting
 sort, on the configurations' expert counts, the Fast-LLM expert-count sweeps
-(4..32 and 64..256), large route counts and the degenerate cases."""
+(4..32 and 64..256), both map forms (one workgroup up to 8192 routes, three
+passes above), large route counts and the degenerate cases."""
 import numpy as np
 import pytest
 import torch
@@ -34,6 +35,16 @@ def test_expert_sweep(oracle_lib, E, skew):
     for S, k in [(1, 1), (7, 2), (1000, min(4, E)), (8192, min(8, E))]:
         ids = wl.gen_random_ids(S, k, E, seed=E * 31 + S, skew=skew)
         check_exact(oracle_lib, ids, E, f"sweep skew={skew}")
+
+
+@pytest.mark.parametrize("E", [8, 1024])
+def test_small_and_general_paths(oracle_lib, E):
+    """Maps of up to 8192 routes run in one workgroup, larger ones in three
+    passes: both sides of that edge, and chunk edges of the one-workgroup
+    form (16 waves of whole 256-route groups)."""
+    for S, k in [(4096, 2), (8192, 1), (8193, 1), (4097, 2), (257, 1), (4095, 2), (4111, 2)]:
+        ids = wl.gen_random_ids(S, k, E, seed=S * 7 + E, skew=1.2)
+        check_exact(oracle_lib, ids, E, "path edge")
 
 
 @pytest.mark.parametrize("name", ["tiny", "mixtral", "gptoss", "dsv3", "qwen2"])
