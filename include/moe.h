@@ -34,7 +34,10 @@
  *    tensors), row-major, 16-byte aligned. bf16 values are passed as their
  *    raw 16-bit patterns (uint16_t).
  *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
- *    enqueues work on it, never synchronises the host and never allocates.
+ *    enqueues kernels on it (no memset or copy nodes: every clear is a
+ *    kernel), never synchronises the host and never allocates, so a sequence
+ *    of calls may be recorded into a HIP graph by stream capture and
+ *    replayed; a replay reads and writes the same buffers.
  *  - The caller owns every buffer. Inputs are read only; outputs are fully
  *    overwritten. `workspace` is caller-allocated scratch whose contents are
  *    undefined before and after a call; calls in flight at the same time

@@ -263,7 +263,13 @@ static void launch_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t st
     prof_begin(stream, kid);
     if constexpr (MODE == kGateUp || MODE == kGateUpSave) {
         switch (bm) {
-            case 256: launch_pp_persistent<256, 128, MODE, 64, 2, 2, true>(p, stream); break;
+            case 256:
+                // short tiles skip missing rows where they are common; with
+                // ~1000 rows per expert the plain loop keeps the workgroups
+                // sharing a weight panel in step (half the HBM re-reads)
+                if (avg < 768) launch_pp_persistent<256, 128, MODE, 64, 2, 2, true>(p, stream);
+                else launch_pp_persistent<256, 128, MODE, 64, 2>(p, stream);
+                break;
             case 192: launch_pp_persistent<192, 128, MODE, 64, 3, 2, true>(p, stream); break;
             case 64: launch_pp_persistent<64, 128, MODE, 64, 3>(p, stream); break;
             default: launch_pp_persistent<32, 128, MODE, 64, 4>(p, stream); break;
