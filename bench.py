@@ -62,6 +62,26 @@ def layer_flops(S, D, F, E, k, with_router=True):
     return 6.0 * S * k * D * F + (2.0 * S * D * E if with_router else 0.0)
 
 
+def roofline_entry(kernel: str, flops: float, nbytes: float, seconds: float, per: str = "launch") -> dict:
+    """Roofline object for one kernel: against the MFMA peak or the HBM peak,
+    whichever floor (flops / peak, bytes / bandwidth) is longer."""
+    if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_BF16_TFLOPS * 1e12):
+        achieved = nbytes / seconds / 1e9
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                f"algorithmic_bytes_per_{per}": nbytes, f"avg_{per}_us": round(seconds * 1e6, 2)}
+    achieved = flops / seconds / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            f"algorithmic_flops_per_{per}": flops, f"avg_{per}_us": round(seconds * 1e6, 2)}
+
+
+def touched_experts(offsets) -> int:
+    """Experts with at least one route, from the map's offsets (read back after timing)."""
+    o = offsets.cpu()
+    return int(((o[1:] - o[:-1]) > 0).sum().item())
+
+
 def load_traffic(workload: str, per_launch_units: float):
     """HBM bytes per launch of the gate+up kernel from committed rocprofv3 PMC
     counters, or None when absent or taken on different kernel sources."""
@@ -165,6 +185,12 @@ def bench_parallel_linear(args, cfg, p):
     y = torch.empty((N, F), dtype=torch.bfloat16, device="cuda")
     g = torch.Generator(device="cuda").manual_seed(7)
     dy = torch.randn((N, F), generator=g, device="cuda").to(torch.bfloat16)
+    Et = touched_experts(offsets)
+    # algorithmic bytes per launch: weights of the touched experts once, the
+    # activations once, outputs once (dW: every expert's fp32 gradient)
+    pl_bytes = {"pl_gemm": Et * D * F * 2.0 + S * D * 2.0 + N * F * 2.0,
+                "pl_dx_gemm": Et * D * F * 2.0 + N * F * 2.0 + N * D * 4.0,
+                "pl_wgrad_gemm": E * D * F * 4.0 + S * D * 2.0 + N * F * 2.0}
     if args.op == "pl_fwd":
         def step():
             smoe.moe_parallel_linear_fwd(x, w, gates, offsets, src, k, False, True, y, ws)
@@ -194,7 +220,6 @@ def bench_parallel_linear(args, cfg, p):
     if dominant is None:
         dominant = max(("pl_dx_gemm", "pl_wgrad_gemm"), key=lambda n: kern[n][0] / kern[n][1])
     dom_ms = kern[dominant][0] / kern[dominant][1]
-    achieved = dom_flops / (dom_ms / 1e3) / 1e12
     rec = {
         "metric": f"ParallelLinear {'forward' if args.op == 'pl_fwd' else 'backward'} TFLOP/s (up-projection)",
         "value": round(flops / (ms / 1e3) / 1e12, 1),
@@ -210,9 +235,7 @@ def bench_parallel_linear(args, cfg, p):
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} ParallelLinear up-projection ({args.op}; scattered in, grouped out, "
                                f"gated)", "S": S, "D_in": D, "D_out": F, "E": E, "k": k},
-        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "algorithmic_flops_per_launch": dom_flops, "avg_launch_us": round(dom_ms * 1e3, 2)},
+        "roofline": roofline_entry(dominant, dom_flops, pl_bytes[dominant], dom_ms / 1e3),
         "kernels": {n: {"avg_us": round(1e3 * tot / c, 2), "launches": c} for n, (tot, c) in kern.items()},
         "wall_s_timed_region": round(wall, 3),
     }
@@ -307,7 +330,15 @@ def bench_ffn_bwd(args, cfg, p, train=False):
     # the GEMM kind with the most time per step (the weight gradients run as two launches per step)
     per_step = {n: kern[n][0] / args.steps for n in gemm_flops if n in kern}
     dominant = max(per_step, key=per_step.get)
-    achieved = gemm_flops[dominant] / (per_step[dominant] / 1e3) / 1e12
+    Et = touched_experts(offsets)
+    w_gu, w_dn = Et * 2.0 * D * F * 2, Et * 1.0 * F * D * 2  # touched W1+W3, W2 (bf16)
+    gemm_bytes = {  # per step: weights once, activations and outputs once
+        "bwd_recompute_gemm": w_gu + S * D * 2.0 + N * 3.0 * F * 2,
+        "ffn_gate_up_gemm": w_gu + S * D * 2.0 + N * 3.0 * F * 2,
+        "bwd_dh_gemm": w_dn + S * D * 2.0 + 2 * N * 2.0 * F * 2,
+        "bwd_wgrad_gemm": E * 3.0 * D * F * 4 + 2 * N * D * 2.0 + N * 3.0 * F * 2,
+        "bwd_dx_gemm": w_gu + N * 2.0 * F * 2 + N * D * 4.0,
+        "ffn_down_scatter_gemm": w_dn + N * F * 2.0 + N * D * 4.0}
     rec = {
         "metric": ("MoE expert-FFN training step TFLOP/s (forward keeping activations + backward)" if train else
                    "MoE expert-FFN backward TFLOP/s (dx, dW1, dW3, dW2, router-weight gradient)"),
@@ -326,10 +357,8 @@ def bench_ffn_bwd(args, cfg, p, train=False):
                                 if train else f"{cfg.name} expert FFN backward (SwiGLU, gate+up recomputed)"),
                    "S": S, "D": D, "F": F, "E": E, "k": k},
         "tokens_per_s": round(S / (ms / 1e3), 1),
-        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "algorithmic_flops_per_step": gemm_flops[dominant],
-                     "avg_step_us": round(per_step[dominant] * 1e3, 2)},
+        "roofline": roofline_entry(dominant, gemm_flops[dominant], gemm_bytes[dominant], per_step[dominant] / 1e3,
+                                   per="step"),
         "kernels": {n: {"avg_us": round(1e3 * tot / c, 2), "launches": c} for n, (tot, c) in kern.items()},
         "wall_s_timed_region": round(wall, 3),
     }
