@@ -101,7 +101,7 @@ FfnBwdPlan ffn_bwd_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
     pl.nn_r = (int)((F + 127) / 128);
     pl.nn_h = (int)((F + pl.bn_b - 1) / pl.bn_b);
     pl.nn_x = (int)((D + bn_x - 1) / bn_x);
-    pl.nparts = pl.nn_h * 4;
+    pl.nparts = pl.nn_h;  // one <h, c> partial per column tile of the dh GEMM and route
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;

@@ -440,6 +440,89 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
         __syncthreads();  // the next tile's DMA may overwrite the staging area
         return;
     }
+    if constexpr (MODE == kSwigluBwd) {
+        // c = dout W2^T is staged through LDS as fp32 rows (as for kDownRows);
+        // then each thread takes 8 consecutive columns of a route row: a and b
+        // come in, da and db go out, as 16-byte accesses, and the row's
+        // <SiLU(a) * b, c> over the tile's columns is summed over the row's
+        // threads into one partial per (column tile, route)
+        constexpr int YS = BN + 4;
+        constexpr int SMEM = PPGeom<BM, BN, MODE, BK, STAGES, STAGES_A>::SMEM;
+        constexpr int PASSES = (BM * YS * 4 <= SMEM) ? 1 : (MT % 2 == 0 && BM / 2 * YS * 4 <= SMEM) ? 2 : MT;
+        static_assert(MT % PASSES == 0 && BM / PASSES * YS * 4 <= SMEM, "staged rows fit the ring");
+        constexpr int MTP = MT / PASSES;
+        constexpr int RP = BM / PASSES;
+        constexpr int TPR = BN / 8;  // threads per row, 8 columns each (a power of two <= 64)
+        static_assert(TPR <= 64 && (TPR & (TPR - 1)) == 0, "a row's threads share one wave");
+        float *sy = reinterpret_cast<float *>(smem);
+        const int c0 = (tid % TPR) * 8;
+        __syncthreads();
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+#pragma unroll
+            for (int il = 0; il < MTP; ++il)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        sy[((WM * il + wm) * 16 + row_grp + r) * YS + wn * WTN + j * 16 + col_in_tile] =
+                            acc[0][ps * MTP + il][j][r];
+            __syncthreads();
+            // every thread of a row runs the same number of iterations (rows
+            // are whole groups of TPR threads), so the shuffles below see all
+            // of the row's lanes
+            for (int rl = tid / TPR; rl < RP; rl += 512 / TPR) {
+                const int slot = row0 + ps * RP + rl;
+                const bool live = slot < row1 && n0 + c0 < N;  // F % 8 == 0: all 8 columns or none
+                float part = 0.f;
+                int f = 0;
+                if (live) {
+                    f = p.slot_src[slot];
+                    const float w = p.gate[f];
+                    uint16_t *ab = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * (2 * N) + n0 + c0;
+                    const uint4 av = *reinterpret_cast<const uint4 *>(ab);
+                    const uint4 bv = *reinterpret_cast<const uint4 *>(ab + N);
+                    const float4 c_lo = *reinterpret_cast<const float4 *>(sy + rl * YS + c0);
+                    const float4 c_hi = *reinterpret_cast<const float4 *>(sy + rl * YS + c0 + 4);
+                    const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+                    const float cc[8] = {c_lo.x, c_lo.y, c_lo.z, c_lo.w, c_hi.x, c_hi.y, c_hi.z, c_hi.w};
+                    uint32_t da[4], db[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint32_t lo_a, hi_a, lo_b, hi_b;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const float a = bf16_bits_to_f32((uint16_t)(aw[q] >> (16 * h)));
+                            const float b = bf16_bits_to_f32((uint16_t)(bw[q] >> (16 * h)));
+                            const float c = cc[2 * q + h];
+                            const float s = 1.0f / (1.0f + __expf(-a));
+                            const float silu = a * s;
+                            part += silu * b * c;
+                            const float dh = w * c;
+                            const uint32_t xa = f32_to_bf16_bits(dh * b * s * (1.0f + a * (1.0f - s)));
+                            const uint32_t xb = f32_to_bf16_bits(dh * silu);
+                            if (h == 0) {
+                                lo_a = xa;
+                                lo_b = xb;
+                            } else {
+                                hi_a = xa;
+                                hi_b = xb;
+                            }
+                        }
+                        da[q] = lo_a | (hi_a << 16);
+                        db[q] = lo_b | (hi_b << 16);
+                    }
+                    *reinterpret_cast<uint4 *>(ab) = make_uint4(da[0], da[1], da[2], da[3]);
+                    *reinterpret_cast<uint4 *>(ab + N) = make_uint4(db[0], db[1], db[2], db[3]);
+                }
+#pragma unroll
+                for (int d = TPR / 2; d >= 1; d >>= 1) part += __shfl_xor(part, d, TPR);
+                if (tid % TPR == 0 && slot < row1) p.part[(size_t)nt * p.M + f] = part;
+            }
+            __syncthreads();
+        }
+        return;
+    }
     if constexpr (MODE == kDownRows) {
         // the fp32 rows are staged through LDS in passes of whole 32-row
         // groups and leave as 16-byte stores of whole tile rows (BN floats of
@@ -538,31 +621,6 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
                         hh[col] = f32_to_bf16_bits(sg * u);
                     }
                 }
-            } else if constexpr (MODE == kSwigluBwd) {
-                const int f = p.slot_src[slot];
-                const float w = p.gate[f];
-                uint16_t *ab = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * (2 * N) + n0;
-                float part = 0.f;
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const int col = wn * WTN + j * 16 + col_in_tile;
-                    if (n0 + col < N) {
-                        const float c = acc[0][i][j][r];
-                        const float a = bf16_bits_to_f32(ab[col]), b = bf16_bits_to_f32(ab[N + col]);
-                        const float s = 1.0f / (1.0f + __expf(-a));
-                        const float silu = a * s;
-                        part += silu * b * c;
-                        const float dh = w * c;
-                        ab[col] = f32_to_bf16_bits(dh * b * s * (1.0f + a * (1.0f - s)));
-                        ab[N + col] = f32_to_bf16_bits(dh * silu);
-                    }
-                }
-                // the 16 lanes of this row group hold the row's columns: sum them
-                part += __shfl_xor(part, 8, 16);
-                part += __shfl_xor(part, 4, 16);
-                part += __shfl_xor(part, 2, 16);
-                part += __shfl_xor(part, 1, 16);
-                if (col_in_tile == 0) p.part[(size_t)(nt * WN + wn) * p.M + f] = part;
             } else if constexpr (MODE == kLinBf16) {
                 const float w = p.gate ? p.gate[p.slot_src[slot]] : 1.0f;
                 uint16_t *yp = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * N + n0;
