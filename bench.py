@@ -190,7 +190,7 @@ def bench_parallel_linear(args, cfg, p):
     # activations once, outputs once (dW: every expert's fp32 gradient)
     pl_bytes = {"pl_gemm": Et * D * F * 2.0 + S * D * 2.0 + N * F * 2.0,
                 "pl_dx_gemm": Et * D * F * 2.0 + N * F * 2.0 + N * D * 4.0,
-                "pl_wgrad_gemm": E * D * F * 4.0 + S * D * 2.0 + N * F * 2.0}
+                "pl_wgrad_gemm": E * D * F * (2.0 if args.dw_bf16 else 4.0) + S * D * 2.0 + N * F * 2.0}
     if args.op == "pl_fwd":
         def step():
             smoe.moe_parallel_linear_fwd(x, w, gates, offsets, src, k, False, True, y, ws)
@@ -198,7 +198,8 @@ def bench_parallel_linear(args, cfg, p):
         dominant, dom_flops = "pl_gemm", 2.0 * N * D * F
     else:
         def step():
-            smoe.moe_parallel_linear_bwd(x, w, gates, offsets, src, dy, k, False, True, workspace=ws)
+            smoe.moe_parallel_linear_bwd(x, w, gates, offsets, src, dy, k, False, True, workspace=ws,
+                                         dw_dtype=torch.bfloat16 if args.dw_bf16 else torch.float32)
         flops = 4.0 * N * D * F  # dx and dw products (dgates is a by-product of the dx rows)
         dominant, dom_flops = None, 2.0 * N * D * F  # the slower of the dx and dw GEMMs
     stream = torch.cuda.current_stream()
@@ -234,7 +235,8 @@ def bench_parallel_linear(args, cfg, p):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} ParallelLinear up-projection ({args.op}; scattered in, grouped out, "
-                               f"gated)", "S": S, "D_in": D, "D_out": F, "E": E, "k": k},
+                               f"gated{', bf16 dW' if args.op == 'pl_bwd' and args.dw_bf16 else ''})", "S": S,
+                   "D_in": D, "D_out": F, "E": E, "k": k},
         "roofline": roofline_entry(dominant, dom_flops, pl_bytes[dominant], dom_ms / 1e3),
         "kernels": {n: {"avg_us": round(1e3 * tot / c, 2), "launches": c} for n, (tot, c) in kern.items()},
         "wall_s_timed_region": round(wall, 3),
@@ -292,6 +294,8 @@ def bench_ffn_bwd(args, cfg, p, train=False):
     ws = torch.empty(smoe.scatter_ffn_bwd_workspace_bytes(S, D, F, E, k), dtype=torch.uint8, device="cuda")
     g = torch.Generator(device="cuda").manual_seed(7)
     dout = (torch.randn((S, D), generator=g, device="cuda") * 0.1).to(torch.bfloat16)
+    dw_dtype = torch.bfloat16 if args.dw_bf16 else torch.float32
+    dw_bytes = 2 if args.dw_bf16 else 4
 
     if train:
         saved = torch.empty(smoe.saved_activations_numel(S, F, k), dtype=torch.bfloat16, device="cuda")
@@ -301,10 +305,11 @@ def bench_ffn_bwd(args, cfg, p, train=False):
         def step():
             smoe.moe_scatter_ffn_fwd(p["x"], p["w1"], p["w3"], p["w2"], gates, offsets, src, out, fws, saved=saved)
             smoe.moe_scatter_ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], gates, offsets, src, dout, workspace=ws,
-                                     saved=saved)
+                                     saved=saved, dw_dtype=dw_dtype)
     else:
         def step():
-            smoe.moe_scatter_ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], gates, offsets, src, dout, workspace=ws)
+            smoe.moe_scatter_ffn_bwd(p["x"], p["w1"], p["w3"], p["w2"], gates, offsets, src, dout, workspace=ws,
+                                     dw_dtype=dw_dtype)
 
     N = S * k
     flops = (18.0 if train else 12.0) * N * D * F
@@ -336,7 +341,7 @@ def bench_ffn_bwd(args, cfg, p, train=False):
         "bwd_recompute_gemm": w_gu + S * D * 2.0 + N * 3.0 * F * 2,
         "ffn_gate_up_gemm": w_gu + S * D * 2.0 + N * 3.0 * F * 2,
         "bwd_dh_gemm": w_dn + S * D * 2.0 + 2 * N * 2.0 * F * 2,
-        "bwd_wgrad_gemm": E * 3.0 * D * F * 4 + 2 * N * D * 2.0 + N * 3.0 * F * 2,
+        "bwd_wgrad_gemm": E * 3.0 * D * F * dw_bytes + 2 * N * D * 2.0 + N * 3.0 * F * 2,
         "bwd_dx_gemm": w_gu + N * 2.0 * F * 2 + N * D * 4.0,
         "ffn_down_scatter_gemm": w_dn + N * F * 2.0 + N * D * 4.0}
     rec = {
@@ -354,7 +359,8 @@ def bench_ffn_bwd(args, cfg, p, train=False):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": (f"{cfg.name} expert FFN training step (forward + backward, saved activations)"
-                                if train else f"{cfg.name} expert FFN backward (SwiGLU, gate+up recomputed)"),
+                                if train else f"{cfg.name} expert FFN backward (SwiGLU, gate+up recomputed)")
+                               + (", bf16 weight gradients" if args.dw_bf16 else ", fp32 weight gradients"),
                    "S": S, "D": D, "F": F, "E": E, "k": k},
         "tokens_per_s": round(S / (ms / 1e3), 1),
         "roofline": roofline_entry(dominant, gemm_flops[dominant], gemm_bytes[dominant], per_step[dominant] / 1e3,
@@ -424,6 +430,8 @@ def main():
     ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "train", "pl_fwd", "pl_bwd", "map_sweep"],
                     help="layer: the MoE forward (default); ffn_bwd: the expert FFN backward; "
                          "pl_fwd / pl_bwd: ParallelLinear up-projection")
+    ap.add_argument("--dw-bf16", action="store_true",
+                    help="ffn_bwd / train / pl_bwd: weight gradients stored as bf16 (the *_bf16w entry points)")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run three device-to-device copies of BYTES (HBM counter calibration)")

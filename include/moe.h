@@ -230,6 +230,22 @@ int moe_scatter_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
                         float *d_topk_weights, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * moe_scatter_ffn_bwd with the weight gradients stored in the weights' own
+ * dtype: dw1, dw3 [E, D, F] and dw2 [E, F, D] are bf16, each element the
+ * fp32 sum of moe_scatter_ffn_bwd rounded once to nearest-even (the same
+ * bits as rounding that call's fp32 result). The reduction is unchanged;
+ * the stores move half the bytes, which is what bounds the weight-gradient
+ * GEMMs of models with many small experts. Everything else (arguments,
+ * workspace, limits, saved_activations, NULL outputs) as moe_scatter_ffn_bwd.
+ */
+int moe_scatter_ffn_bwd_bf16w(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                              const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                              const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k,
+                              uint16_t *saved_activations, uint16_t *dx, uint16_t *dw1, uint16_t *dw3,
+                              uint16_t *dw2, float *d_topk_weights, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
  * Workspace bytes of moe_parallel_linear_fwd and moe_parallel_linear_bwd for
  * these sizes (one size serves every grouping mode and both calls): tile
  * tables, fp32 rows [S*k, max(D_in, D_out)] and the bf16 slot-order rows the
@@ -284,6 +300,17 @@ int moe_parallel_linear_bwd(const uint16_t *x, const uint16_t *w, const float *g
                             const int32_t *slot_src, const uint16_t *dy, int32_t S, int32_t k, int32_t D_in,
                             int32_t D_out, int32_t E, int32_t grouped_in, int32_t grouped_out, uint16_t *dx,
                             float *dw, float *dgates, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_parallel_linear_bwd with dw [E, D_in, D_out] stored as bf16: each
+ * element is that call's fp32 sum rounded once to nearest-even. Everything
+ * else as moe_parallel_linear_bwd.
+ */
+int moe_parallel_linear_bwd_bf16w(const uint16_t *x, const uint16_t *w, const float *gates,
+                                  const int32_t *expert_offsets, const int32_t *slot_src, const uint16_t *dy,
+                                  int32_t S, int32_t k, int32_t D_in, int32_t D_out, int32_t E, int32_t grouped_in,
+                                  int32_t grouped_out, uint16_t *dx, uint16_t *dw, float *dgates, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /*
  * Profiling hooks (measurement support, not part of the method). While

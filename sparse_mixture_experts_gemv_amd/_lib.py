@@ -36,11 +36,15 @@ SIGNATURES = {
                                                  _P, _SZ, _P]),
     "moe_scatter_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
                                            _P, _P, _P, _P, _SZ, _P]),
+    "moe_scatter_ffn_bwd_bf16w": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P,
+                                                 _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_parallel_linear_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_parallel_linear_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                                _SZ, _P]),
     "moe_parallel_linear_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P,
                                                _P, _P, _P, _SZ, _P]),
+    "moe_parallel_linear_bwd_bf16w": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                     _P, _P, _P, _P, _SZ, _P]),
     "moe_profile_start": (ctypes.c_int, [ctypes.c_int]),
     "moe_profile_stop": (ctypes.c_int, []),
     "moe_profile_kinds": (ctypes.c_int, []),
@@ -230,10 +234,15 @@ def scatter_ffn_bwd_workspace_bytes(S: int, D: int, F: int, E: int, k: int) -> i
 def moe_scatter_ffn_bwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
                         topk_weights: torch.Tensor, expert_offsets: torch.Tensor, slot_src: torch.Tensor,
                         dout: torch.Tensor, need=("dx", "dw1", "dw3", "dw2", "dg"),
-                        workspace: Optional[torch.Tensor] = None, stream=None, saved: Optional[torch.Tensor] = None):
-    """Backward of moe_scatter_ffn_fwd -> dict with dx bf16 [S, D], dw1 / dw3 fp32 [E, D, F],
-    dw2 fp32 [E, F, D] and dg fp32 [S, k] (the router-weight gradient), for the names in `need`.
-    saved: the buffer of the training-mode forward (skips the recomputation; overwritten)."""
+                        workspace: Optional[torch.Tensor] = None, stream=None, saved: Optional[torch.Tensor] = None,
+                        dw_dtype=torch.float32):
+    """Backward of moe_scatter_ffn_fwd -> dict with dx bf16 [S, D], dw1 / dw3 [E, D, F],
+    dw2 [E, F, D] and dg fp32 [S, k] (the router-weight gradient), for the names in `need`.
+    dw_dtype: torch.float32 (moe_scatter_ffn_bwd) or torch.bfloat16 (moe_scatter_ffn_bwd_bf16w:
+    the same sums rounded once). saved: the buffer of the training-mode forward (skips the
+    recomputation; overwritten)."""
+    if dw_dtype not in (torch.float32, torch.bfloat16):
+        raise MoEError("dw_dtype must be torch.float32 or torch.bfloat16")
     S, D = x.shape
     E, D2, F = w1.shape
     k = topk_weights.shape[1]
@@ -248,14 +257,15 @@ def moe_scatter_ffn_bwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2:
     if saved is not None:
         _dev(saved, torch.bfloat16, "saved", (saved_activations_numel(S, F, k),))
     dev = x.device
-    shapes = dict(dx=((S, D), torch.bfloat16), dw1=((E, D, F), torch.float32), dw3=((E, D, F), torch.float32),
-                  dw2=((E, F, D), torch.float32), dg=((S, k), torch.float32))
+    shapes = dict(dx=((S, D), torch.bfloat16), dw1=((E, D, F), dw_dtype), dw3=((E, D, F), dw_dtype),
+                  dw2=((E, F, D), dw_dtype), dg=((S, k), torch.float32))
     out = {n: torch.empty(shapes[n][0], dtype=shapes[n][1], device=dev) for n in need}
     ws = _workspace(scatter_ffn_bwd_workspace_bytes(S, D, F, E, k), dev, workspace)
-    _check(load().moe_scatter_ffn_bwd(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(topk_weights),
-                                      _ptr(expert_offsets), _ptr(slot_src), _ptr(dout), S, D, F, E, k, _ptr(saved),
-                                      *(_ptr(out.get(n)) for n in ("dx", "dw1", "dw3", "dw2", "dg")), _ptr(ws),
-                                      ws.numel() * ws.element_size(), _stream(stream)), "moe_scatter_ffn_bwd")
+    name = "moe_scatter_ffn_bwd" if dw_dtype == torch.float32 else "moe_scatter_ffn_bwd_bf16w"
+    _check(getattr(load(), name)(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(topk_weights),
+                                 _ptr(expert_offsets), _ptr(slot_src), _ptr(dout), S, D, F, E, k, _ptr(saved),
+                                 *(_ptr(out.get(n)) for n in ("dx", "dw1", "dw3", "dw2", "dg")), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)), name)
     return out
 
 
@@ -301,23 +311,26 @@ def moe_parallel_linear_bwd(x: torch.Tensor, w: torch.Tensor, gates: Optional[to
                             expert_offsets: torch.Tensor, slot_src: torch.Tensor, dy: torch.Tensor, k: int,
                             grouped_in: bool = False, grouped_out: bool = False, need_dx: bool = True,
                             need_dw: bool = True, need_dgates: bool = True, workspace: Optional[torch.Tensor] = None,
-                            stream=None):
-    """Backward of ParallelLinear -> (dx bf16 like x, dw fp32 [E, D_in, D_out], dgates fp32 [S, k]);
-    an output not requested is None."""
+                            stream=None, dw_dtype=torch.float32):
+    """Backward of ParallelLinear -> (dx bf16 like x, dw [E, D_in, D_out] of dw_dtype (fp32, or bf16:
+    the same sums rounded once), dgates fp32 [S, k]); an output not requested is None."""
+    if dw_dtype not in (torch.float32, torch.bfloat16):
+        raise MoEError("dw_dtype must be torch.float32 or torch.bfloat16")
     S, E, D_in, D_out = _pl_shapes(x, w, expert_offsets, slot_src, k, grouped_in)
     if gates is not None:
         _dev(gates, torch.float32, "gates", (S, k))
     _dev(dy, torch.bfloat16, "dy", ((S * k if grouped_out else S), D_out))
     dev = x.device
     dx = torch.empty_like(x) if need_dx else None
-    dw = torch.empty((E, D_in, D_out), dtype=torch.float32, device=dev) if need_dw else None
+    dw = torch.empty((E, D_in, D_out), dtype=dw_dtype, device=dev) if need_dw else None
     dg = torch.empty((S, k), dtype=torch.float32, device=dev) if need_dgates else None
     need = parallel_linear_workspace_bytes(S, k, D_in, D_out, E)
     ws = _workspace(need, dev, workspace)
-    _check(load().moe_parallel_linear_bwd(_ptr(x), _ptr(w), _ptr(gates), _ptr(expert_offsets), _ptr(slot_src),
-                                          _ptr(dy), S, k, D_in, D_out, E, int(grouped_in), int(grouped_out),
-                                          _ptr(dx), _ptr(dw), _ptr(dg), _ptr(ws), ws.numel() * ws.element_size(),
-                                          _stream(stream)), "moe_parallel_linear_bwd")
+    name = "moe_parallel_linear_bwd" if dw_dtype == torch.float32 else "moe_parallel_linear_bwd_bf16w"
+    _check(getattr(load(), name)(_ptr(x), _ptr(w), _ptr(gates), _ptr(expert_offsets), _ptr(slot_src),
+                                 _ptr(dy), S, k, D_in, D_out, E, int(grouped_in), int(grouped_out),
+                                 _ptr(dx), _ptr(dw), _ptr(dg), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)), name)
     return dx, dw, dg
 
 

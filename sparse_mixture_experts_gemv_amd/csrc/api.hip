@@ -141,11 +141,13 @@ size_t moe_scatter_ffn_bwd_workspace_bytes(int32_t S, int32_t D, int32_t F, int3
     return smoe::ffn_bwd_plan(S, D, F, E, k).ws_bytes;
 }
 
-int moe_scatter_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
-                        const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
-                        const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k,
-                        uint16_t *saved_activations, uint16_t *dx, float *dw1, float *dw3, float *dw2,
-                        float *d_topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+int ffn_bwd_impl(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                 const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                 const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k,
+                 uint16_t *saved_activations, uint16_t *dx, void *dw1, void *dw3, void *dw2, bool dw_bf16,
+                 float *d_topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
     if (S < 0 || D < 1 || F < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
     if (!dx && !dw1 && !dw3 && !dw2 && !d_topk_weights) return MOE_ERR_INVALID_ARGUMENT;
     if (!w1 || !w3 || !w2 || !expert_offsets || !workspace) return MOE_ERR_INVALID_ARGUMENT;
@@ -165,8 +167,31 @@ int moe_scatter_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w
     if (workspace_bytes < pl.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (S == 0 && !dw1 && !dw3 && !dw2) return MOE_OK;  // with a weight gradient requested, zeros are written
     return finish(smoe::launch_ffn_bwd(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, dout, S, D, F, E, k,
-                                       saved_activations, dx, dw1, dw3, dw2, d_topk_weights, workspace,
+                                       saved_activations, dx, dw1, dw3, dw2, dw_bf16, d_topk_weights, workspace,
                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int moe_scatter_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                        const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                        const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k,
+                        uint16_t *saved_activations, uint16_t *dx, float *dw1, float *dw3, float *dw2,
+                        float *d_topk_weights, void *workspace, size_t workspace_bytes, void *stream) {
+    return ffn_bwd_impl(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, dout, S, D, F, E, k,
+                        saved_activations, dx, dw1, dw3, dw2, false, d_topk_weights, workspace, workspace_bytes,
+                        stream);
+}
+
+int moe_scatter_ffn_bwd_bf16w(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                              const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
+                              const uint16_t *dout, int32_t S, int32_t D, int32_t F, int32_t E, int32_t k,
+                              uint16_t *saved_activations, uint16_t *dx, uint16_t *dw1, uint16_t *dw3,
+                              uint16_t *dw2, float *d_topk_weights, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    return ffn_bwd_impl(x, w1, w3, w2, topk_weights, expert_offsets, slot_src, dout, S, D, F, E, k,
+                        saved_activations, dx, dw1, dw3, dw2, true, d_topk_weights, workspace, workspace_bytes,
+                        stream);
 }
 
 size_t moe_parallel_linear_workspace_bytes(int32_t S, int32_t k, int32_t D_in, int32_t D_out, int32_t E) {
@@ -215,10 +240,12 @@ int moe_parallel_linear_fwd(const uint16_t *x, const uint16_t *w, const float *g
                                       grouped_out != 0, y, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int moe_parallel_linear_bwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
-                            const int32_t *slot_src, const uint16_t *dy, int32_t S, int32_t k, int32_t D_in,
-                            int32_t D_out, int32_t E, int32_t grouped_in, int32_t grouped_out, uint16_t *dx,
-                            float *dw, float *dgates, void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+int pl_bwd_impl(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
+                const int32_t *slot_src, const uint16_t *dy, int32_t S, int32_t k, int32_t D_in, int32_t D_out,
+                int32_t E, int32_t grouped_in, int32_t grouped_out, uint16_t *dx, void *dw, bool dw_bf16,
+                float *dgates, void *workspace, size_t workspace_bytes, void *stream) {
     if (S < 0 || k < 1 || E < 1 || k > E || D_in < 1 || D_out < 1) return MOE_ERR_INVALID_ARGUMENT;
     if (!dx && !dw && !dgates) return MOE_ERR_INVALID_ARGUMENT;
     if (S == 0 && !dw) return MOE_OK;  // with dw, the zero gradient is still written
@@ -229,8 +256,27 @@ int moe_parallel_linear_bwd(const uint16_t *x, const uint16_t *w, const float *g
                             workspace, workspace_bytes);
     if (st != MOE_OK) return st;
     return finish(smoe::launch_pl_bwd(x, w, gates, expert_offsets, slot_src, dy, S, k, D_in, D_out, E,
-                                      grouped_in != 0, grouped_out != 0, dx, dw, dgates, workspace,
+                                      grouped_in != 0, grouped_out != 0, dx, dw, dw_bf16, dgates, workspace,
                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int moe_parallel_linear_bwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
+                            const int32_t *slot_src, const uint16_t *dy, int32_t S, int32_t k, int32_t D_in,
+                            int32_t D_out, int32_t E, int32_t grouped_in, int32_t grouped_out, uint16_t *dx,
+                            float *dw, float *dgates, void *workspace, size_t workspace_bytes, void *stream) {
+    return pl_bwd_impl(x, w, gates, expert_offsets, slot_src, dy, S, k, D_in, D_out, E, grouped_in, grouped_out, dx,
+                       dw, false, dgates, workspace, workspace_bytes, stream);
+}
+
+int moe_parallel_linear_bwd_bf16w(const uint16_t *x, const uint16_t *w, const float *gates,
+                                  const int32_t *expert_offsets, const int32_t *slot_src, const uint16_t *dy,
+                                  int32_t S, int32_t k, int32_t D_in, int32_t D_out, int32_t E, int32_t grouped_in,
+                                  int32_t grouped_out, uint16_t *dx, uint16_t *dw, float *dgates, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return pl_bwd_impl(x, w, gates, expert_offsets, slot_src, dy, S, k, D_in, D_out, E, grouped_in, grouped_out, dx,
+                       dw, true, dgates, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -162,7 +162,8 @@ static void launch_bwd_bt(int bm, int64_t avg, const GemmParams &p, hipStream_t 
 hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                           const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
                           const uint16_t *dout, int S, int D, int F, int E, int k, uint16_t *saved, uint16_t *dx,
-                          float *dw1, float *dw3, float *dw2, float *dg, void *workspace, hipStream_t stream) {
+                          void *dw1, void *dw3, void *dw2, bool dw_bf16, float *dg, void *workspace,
+                          hipStream_t stream) {
     const FfnBwdPlan pl = ffn_bwd_plan(S, D, F, E, k);
     char *ws = reinterpret_cast<char *>(workspace);
     const int N = S * k;
@@ -270,6 +271,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
         q.B0 = dyg;
         q.offsets = expert_offsets;
         q.C0 = dw2;
+        q.out_bf16 = dw_bf16;
         q.M = F;
         q.N = D;
         q.E = E;
@@ -289,6 +291,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
         q.offsets = expert_offsets;
         q.C0 = dw1 ? dw1 : dw3;
         q.C1 = dw3 ? dw3 : dw1;
+        q.out_bf16 = dw_bf16;
         q.M = D;
         q.N = F;
         q.E = E;

@@ -31,7 +31,8 @@ struct WgradParams {
     const uint16_t *A;        // [rows, M] slot order
     const uint16_t *B0, *B1;  // [rows, N] slot order, row stride ldb (B1 only when NB = 2)
     const int32_t *offsets;   // [E + 1] expert row ranges
-    float *C0, *C1;           // [E, M, N]
+    void *C0, *C1;            // [E, M, N] fp32, or bf16 with out_bf16
+    int out_bf16;             // store the fp32 tile sums rounded to bf16 (RNE)
     int M, N, E;
     int ldb;                  // row stride of B0 / B1 in elements (>= N)
     int n_mt, n_nt;           // tiles per expert
@@ -236,7 +237,7 @@ __device__ __forceinline__ void wg_tile(const WgradParams &p, char *smem, int e,
     __syncthreads();  // every wave is done reading the operand ring
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        float *C = (b == 0 ? p.C0 : p.C1) + (size_t)e * M * N;
+        const size_t c_off = (size_t)e * M * N;
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
@@ -253,7 +254,18 @@ __device__ __forceinline__ void wg_tile(const WgradParams &p, char *smem, int e,
                 const int n = n0 + wn * WTN + rd_col;
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(reg + rl * STRIDE + rd_col);
                 // streaming store: the gradient is not read again by this pass
-                if (m < M && n < N) __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(C + (size_t)m * N + n));
+                if (m < M && n < N) {
+                    const size_t o = c_off + (size_t)m * N + n;
+                    if (p.out_bf16) {
+                        const u32x2 w2 = {(uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
+                                          (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
+                        __builtin_nontemporal_store(w2, reinterpret_cast<u32x2 *>(
+                                                            static_cast<uint16_t *>(b == 0 ? p.C0 : p.C1) + o));
+                    } else {
+                        __builtin_nontemporal_store(
+                            v, reinterpret_cast<f32x4 *>(static_cast<float *>(b == 0 ? p.C0 : p.C1) + o));
+                    }
+                }
             }
         }
     }

@@ -83,7 +83,7 @@ hipError_t launch_pl_fwd(const uint16_t *x, const uint16_t *w, const float *gate
                          bool grouped_out, uint16_t *y, void *workspace, hipStream_t stream);
 hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
                          const int32_t *slot_src, const uint16_t *dy, int S, int k, int D_in, int D_out, int E,
-                         bool grouped_in, bool grouped_out, uint16_t *dx, float *dw, float *dgates,
+                         bool grouped_in, bool grouped_out, uint16_t *dx, void *dw, bool dw_bf16, float *dgates,
                          void *workspace, hipStream_t stream);
 
 // ---- expert FFN backward ----
@@ -103,7 +103,8 @@ inline bool ffn_bwd_plan_fits(const FfnBwdPlan &pl) {
 hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                           const float *topk_weights, const int32_t *expert_offsets, const int32_t *slot_src,
                           const uint16_t *dout, int S, int D, int F, int E, int k, uint16_t *saved, uint16_t *dx,
-                          float *dw1, float *dw3, float *dw2, float *dg, void *workspace, hipStream_t stream);
+                          void *dw1, void *dw3, void *dw2, bool dw_bf16, float *dg, void *workspace,
+                          hipStream_t stream);
 
 // ---- router ----
 size_t route_ws_bytes(int64_t S, int64_t E);

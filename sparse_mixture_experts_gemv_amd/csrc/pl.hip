@@ -273,7 +273,7 @@ hipError_t launch_pl_fwd(const uint16_t *x, const uint16_t *w, const float *gate
 
 hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gates, const int32_t *expert_offsets,
                          const int32_t *slot_src, const uint16_t *dy, int S, int k, int D_in, int D_out, int E,
-                         bool grouped_in, bool grouped_out, uint16_t *dx, float *dw, float *dgates,
+                         bool grouped_in, bool grouped_out, uint16_t *dx, void *dw, bool dw_bf16, float *dgates,
                          void *workspace, hipStream_t stream) {
     const PlPlan pl = pl_plan(S, k, D_in, D_out, E);
     char *ws = reinterpret_cast<char *>(workspace);
@@ -330,6 +330,7 @@ hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gate
         q.B1 = nullptr;
         q.offsets = expert_offsets;
         q.C0 = dw;
+        q.out_bf16 = dw_bf16;
         q.C1 = nullptr;
         q.M = D_in;
         q.N = D_out;

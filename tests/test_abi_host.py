@@ -22,13 +22,13 @@ def lib():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
     import sparse_mixture_experts_gemv_amd._lib as b
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.SIGNATURES)
@@ -112,6 +112,10 @@ def test_parallel_linear_validation(lib):
     assert bwd(*ba(dw=MISALIGNED)) == 1
     assert bwd(*ba(ws=4096)) == 3
     assert bwd(*ba(S=0, dw=None)) == 0              # nothing to write
+    bb = lib.moe_parallel_linear_bwd_bf16w
+    assert bb(*ba(dx=None, dw=None, dg=None)) == 1
+    assert bb(*ba(dw=MISALIGNED)) == 1
+    assert bb(*ba(ws=4096)) == 3
     n = lib.moe_parallel_linear_workspace_bytes(4096, 2, 4096, 14336, 8)
     # fp32 rows [S*k, max(D_in, D_out)] + bf16 slot-order copies of x and g*dy + small tables
     base = 8192 * 14336 * 4 + 8192 * 4096 * 2 + 8192 * 14336 * 2
@@ -131,6 +135,12 @@ def test_ffn_bwd_validation(lib):
     assert b(*args(E=2048)) == 2
     assert b(*args(ws=4096)) == 3
     assert b(*args(sv=MISALIGNED)) == 1
+    # the bf16-weight-gradient form shares every check
+    bb = lib.moe_scatter_ffn_bwd_bf16w
+    assert bb(*args(k=9)) == 1
+    assert bb(*args(tw=None)) == 1
+    assert bb(*args(F=80)) == 2
+    assert bb(*args(ws=4096)) == 3
     t = lib.moe_scatter_ffn_fwd_train
     targs = lambda S=16, D=64, F=128, E=8, k=2, ws=1 << 30, sv=FAKE: (
         FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, S, D, F, E, k, FAKE, sv, FAKE, ws, None)

@@ -100,6 +100,28 @@ def test_ffn_bwd_small_all_elements(oracle_lib, S, D, F, E, k, skew):
     dg_close(got["dg"].cpu().numpy().astype(np.float64), ref["dg"], f"dg {tag}")
 
 
+@pytest.mark.parametrize("idx", [0, 2, 4, 5])
+def test_ffn_bwd_bf16_weight_gradients(oracle_lib, idx):
+    """moe_scatter_ffn_bwd_bf16w: dw1, dw3, dw2 are the fp32 call's rounded to bf16 (RNE), bit for
+    bit; dx and dg are the fp32 call's; the bf16 gradients are within the bar of the fp64 oracle."""
+    import sparse_mixture_experts_gemv_amd as smoe
+    S, D, F, E, k, skew = SMALL[idx]
+    p, ids, w, dout = problem(S, D, F, E, k, skew, seed=S + D + F)
+    _, offsets, _, src = smoe.moe_sparse_map(torch.from_numpy(ids).to(DEV), E)
+    args = (p["x"], p["w1"], p["w3"], p["w2"], torch.from_numpy(w).to(DEV), offsets, src, dout)
+    g32 = smoe.moe_scatter_ffn_bwd(*args)
+    g16 = smoe.moe_scatter_ffn_bwd(*args, dw_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for n in ("dw1", "dw3", "dw2"):
+        assert g16[n].dtype == torch.bfloat16
+        assert torch.equal(g16[n], g32[n].to(torch.bfloat16)), n
+    assert torch.equal(g16["dx"], g32["dx"]) and torch.equal(g16["dg"], g32["dg"])
+    ref = oracle_lib.ffn_bwd(bits(p["x"]), bits(p["w1"]), bits(p["w3"]), bits(p["w2"]), ids, w.astype(np.float64),
+                             bits(dout), want=("dw1", "dw3", "dw2"))
+    for n in ("dw1", "dw3", "dw2"):
+        grad_close(g16[n].float().cpu().numpy(), ref[n], f"{n} bf16 {S}x{D}x{F} E={E} k={k}")
+
+
 def test_ffn_bwd_subsets_and_reproducible(oracle_lib):
     """Any subset of the outputs equals the full call bit for bit, and calls repeat exactly."""
     p, ids, w, dout = problem(600, 128, 192, 8, 2, None, seed=9)

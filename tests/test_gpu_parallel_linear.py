@@ -118,6 +118,29 @@ def test_parallel_linear_bwd_partial_outputs_and_reproducible(oracle_lib):
     assert torch.equal(full[0], only_dx) and torch.equal(full[1], only_dw) and torch.equal(full[2], only_dg)
 
 
+@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[4], SHAPES[6]], ids=["128rows", "32rows_zipf", "empty_experts"])
+def test_parallel_linear_bwd_bf16_dw(oracle_lib, shape):
+    """moe_parallel_linear_bwd_bf16w: dw is the fp32 call's dw rounded to bf16 (RNE), bit for bit;
+    dx and dgates are the fp32 call's; dw is also within the bar of the fp64 oracle."""
+    import sparse_mixture_experts_gemv_amd as smoe
+    S, k, D_in, D_out, E, skew = shape
+    p = pl_problem(S, k, D_in, D_out, E, skew, False, True, seed=11 * S + E)
+    offsets, src = gpu_map(p["ids"], E)
+    args = (p["x"].to(DEV), p["w"].to(DEV), p["gates"].to(DEV), offsets, src, p["dy"].to(DEV), k, False, True)
+    dx32, dw32, dg32 = smoe.moe_parallel_linear_bwd(*args)
+    dx16, dw16, dg16 = smoe.moe_parallel_linear_bwd(*args, dw_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert dw16.dtype == torch.bfloat16
+    assert torch.equal(dw16, dw32.to(torch.bfloat16))
+    assert torch.equal(dx16, dx32) and torch.equal(dg16, dg32)
+    _, rdw, _ = oracle_lib.parallel_linear_bwd(bits(p["x"]), bits(p["w"]), p["ids"], bits(p["dy"]),
+                                               p["gates"].double().numpy(), False, True)
+    used = np.unique(p["ids"])
+    got = dw16.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.delete(got, used, axis=0) == 0.0)
+    assert_close(got[used].reshape(-1, D_out), rdw[used].reshape(-1, D_out), f"dw bf16 {shape}", configured=False)
+
+
 def test_parallel_linear_bwd_no_tokens_zeroes_dw():
     """S = 0: the weight gradient is written as zeros."""
     import sparse_mixture_experts_gemv_amd as smoe
