@@ -577,18 +577,9 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
             const int row = (WM * i + wm) * 16 + row_grp + r;
             const int slot = row0 + row;
             if (slot >= row1) continue;
-            if constexpr (MODE == kGateUp) {
-                uint16_t *h = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * N + n0;
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const int col = wn * WTN + j * 16 + col_in_tile;
-                    if (n0 + col < N) {
-                        const float g = acc[0][i][j][r], u = acc[1][i][j][r];
-                        const float sg = g / (1.0f + __expf(-g));
-                        h[col] = f32_to_bf16_bits(sg * u);
-                    }
-                }
-            } else if constexpr (MODE == kDown) {
+            // the remaining modes: the atomic down GEMM and the router logits
+            // (every other mode returned from its staged epilogue above)
+            if constexpr (MODE == kDown) {
                 const int f = p.slot_src[slot];
                 const int tok = f / p.topk;
                 const float w = p.gate[f];
@@ -597,37 +588,6 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
                 for (int j = 0; j < NT; ++j) {
                     const int col = wn * WTN + j * 16 + col_in_tile;
                     if (n0 + col < N) atomicAdd(accp + col, w * acc[0][i][j][r]);
-                }
-            } else if constexpr (MODE == kDownRows) {
-                const int f = p.slot_src[slot];
-                const float w = p.gate ? p.gate[f] : 1.0f;
-                float *yp = reinterpret_cast<float *>(p.C) + (size_t)f * N + n0;
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const int col = wn * WTN + j * 16 + col_in_tile;
-                    if (n0 + col < N) yp[col] = w * acc[0][i][j][r];
-                }
-            } else if constexpr (MODE == kGateUpSave) {
-                uint16_t *ab = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * (2 * N) + n0;
-                uint16_t *hh = reinterpret_cast<uint16_t *>(p.C2) + (size_t)slot * N + n0;
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const int col = wn * WTN + j * 16 + col_in_tile;
-                    if (n0 + col < N) {
-                        const float g = acc[0][i][j][r], u = acc[1][i][j][r];
-                        const float sg = g / (1.0f + __expf(-g));  // as the forward kernel
-                        ab[col] = f32_to_bf16_bits(g);
-                        ab[N + col] = f32_to_bf16_bits(u);
-                        hh[col] = f32_to_bf16_bits(sg * u);
-                    }
-                }
-            } else if constexpr (MODE == kLinBf16) {
-                const float w = p.gate ? p.gate[p.slot_src[slot]] : 1.0f;
-                uint16_t *yp = reinterpret_cast<uint16_t *>(p.C) + (size_t)slot * N + n0;
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    const int col = wn * WTN + j * 16 + col_in_tile;
-                    if (n0 + col < N) yp[col] = f32_to_bf16_bits(w * acc[0][i][j][r]);
                 }
             } else {
                 float *out = reinterpret_cast<float *>(p.C) + (size_t)slot * N + n0;
