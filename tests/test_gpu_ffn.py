@@ -35,6 +35,7 @@ def routing_for(p, seed):
 
 
 SMALL = [  # (S, D, F, E, k): tile height picked from S*k/E
+    (2000, 128, 320, 4, 2),    # 1000 rows/expert -> 256-row tiles, short tiles ordered last, F ragged
     (1000, 192, 320, 8, 2),    # 250 rows/expert -> 256-row tiles, F ragged
     (600, 128, 192, 8, 2),     # 150 -> 192-row tiles
     (300, 128, 192, 8, 2),     # 75 -> 64-row tiles
