@@ -135,8 +135,9 @@ def test_ffn_bwd_subsets_and_reproducible(oracle_lib):
             assert torch.equal(part[n], full[n]), (need, n)
 
 
-def test_ffn_bwd_no_tokens():
-    """S = 0 with weight gradients requested: they are written as zeros."""
+@pytest.mark.parametrize("dw_dtype", [torch.float32, torch.bfloat16])
+def test_ffn_bwd_no_tokens(dw_dtype):
+    """S = 0 with weight gradients requested: they are written as zeros (fp32 or bf16)."""
     import sparse_mixture_experts_gemv_amd as smoe
     E, D, F, k = 4, 64, 128, 2
     w1 = torch.randn(E, D, F, device=DEV).to(torch.bfloat16)
@@ -144,9 +145,10 @@ def test_ffn_bwd_no_tokens():
     z = lambda *s, dt=torch.bfloat16: torch.empty(s, dtype=dt, device=DEV)
     offsets = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
     out = smoe.moe_scatter_ffn_bwd(z(0, D), w1, w1, w2, z(0, k, dt=torch.float32), offsets, z(0, dt=torch.int32),
-                                   z(0, D), need=("dw1", "dw3", "dw2"))
+                                   z(0, D), need=("dw1", "dw3", "dw2"), dw_dtype=dw_dtype)
     torch.cuda.synchronize()
     for n in ("dw1", "dw3", "dw2"):
+        assert out[n].dtype == dw_dtype
         assert torch.count_nonzero(out[n]).item() == 0
 
 

@@ -141,8 +141,9 @@ def test_parallel_linear_bwd_bf16_dw(oracle_lib, shape):
     assert_close(got[used].reshape(-1, D_out), rdw[used].reshape(-1, D_out), f"dw bf16 {shape}", configured=False)
 
 
-def test_parallel_linear_bwd_no_tokens_zeroes_dw():
-    """S = 0: the weight gradient is written as zeros."""
+@pytest.mark.parametrize("dw_dtype", [torch.float32, torch.bfloat16])
+def test_parallel_linear_bwd_no_tokens_zeroes_dw(dw_dtype):
+    """S = 0: the weight gradient is written as zeros (fp32 or bf16)."""
     import sparse_mixture_experts_gemv_amd as smoe
     E, D_in, D_out, k = 4, 64, 128, 2
     w = torch.randn(E, D_in, D_out, device=DEV).to(torch.bfloat16)
@@ -150,8 +151,10 @@ def test_parallel_linear_bwd_no_tokens_zeroes_dw():
     dy = torch.empty((0, D_out), dtype=torch.bfloat16, device=DEV)
     offsets = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
     src = torch.empty(0, dtype=torch.int32, device=DEV)
-    _, dw, _ = smoe.moe_parallel_linear_bwd(x, w, None, offsets, src, dy, k, need_dx=False, need_dgates=False)
+    _, dw, _ = smoe.moe_parallel_linear_bwd(x, w, None, offsets, src, dy, k, need_dx=False, need_dgates=False,
+                                            dw_dtype=dw_dtype)
     torch.cuda.synchronize()
+    assert dw.dtype == dw_dtype
     assert dw.shape == (E, D_in, D_out) and torch.count_nonzero(dw).item() == 0
 
 
