@@ -58,6 +58,28 @@ def test_ffn_small_all_tokens(oracle_lib, S, D, F, E, k, atomic):
     assert_close(got, ref, f"ffn {S}x{D}x{F} E={E} k={k} {'atomic' if atomic else 'rows'}", configured=False)
 
 
+DECODE = [  # (S, D, F, E, k, skew): decode-sized batches on 32-row tiles, every token checked
+    (8, 256, 384, 16, 4, None),
+    (5, 128, 192, 4, 2, None),      # every expert holds several of the 5 tokens
+    (8, 2880, 2880, 128, 4, None),  # GPT-OSS widths (ragged against 128- and 256-column tiles)
+    (3, 4096, 14336, 8, 2, None),   # Mixtral widths
+    (8, 3584, 2560, 64, 8, 1.2),    # Qwen2 widths, skewed: the hot experts hold up to 8 rows
+    (1, 64, 64, 8, 2, None),        # one token, a single tile per GEMM
+]
+
+
+@pytest.mark.parametrize("atomic", [False, True], ids=["rows", "atomic"])
+@pytest.mark.parametrize("S,D,F,E,k,skew", DECODE)
+def test_ffn_decode_sizes_all_tokens(oracle_lib, S, D, F, E, k, skew, atomic):
+    cfg = wl.MoEConfig("decode", 70 + E + k, S, D, F, E, k, None)
+    p = make_problem(cfg)
+    ids = wl.gen_random_ids(S, k, E, seed=S * 31 + E, skew=skew)
+    w = np.random.default_rng(S + E).dirichlet(np.ones(k), size=S).astype(np.float32)
+    got = gpu_ffn(p, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), atomic)
+    ref = oracle_ffn_rows(oracle_lib, p, ids, w, np.arange(S))
+    assert_close(got, ref, f"decode ffn {S}x{D}x{F} E={E} k={k} {'atomic' if atomic else 'rows'}", configured=False)
+
+
 @pytest.mark.parametrize("atomic", [False, True], ids=["rows", "atomic"])
 def test_ffn_skewed_single_expert(oracle_lib, atomic):
     """All routes on two experts: one expert spans many M tiles, the rest are empty."""
@@ -102,10 +124,10 @@ def test_ffn_short_tiles_row_edges(oracle_lib, family, atomic):
     assert_close(got, ref, f"short-tile row edges ({family}) {'atomic' if atomic else 'rows'}", configured=False)
 
 
-@pytest.mark.parametrize("S", [500, 40])
+@pytest.mark.parametrize("S", [500, 40, 8])
 def test_ffn_rows_combine_is_bitwise_reproducible(S):
     """The ordered combine gives the same bits on every call, also for k = 8
-    and for decode-sized batches (S = 40: 5 rows per expert, 32-row tiles)."""
+    and for small batches (S = 40 and S = 8: 32-row tiles)."""
     cfg = wl.MoEConfig("repro", 62, S, 256, 192, 64, 8, None)
     p = make_problem(cfg)
     ids, w = routing_for(p, seed=5)
