@@ -99,7 +99,11 @@ __device__ __forceinline__ int pp_b_swz(int k) {
 template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES>
 struct PPGeom {
     static constexpr int NB = (MODE == kGateUp || MODE == kGateUpSave) ? 2 : 1;
-    static constexpr int SMEM = STAGES_A * BM * BK * 2 + STAGES * NB * BK * BN * 2;
+    static constexpr int RING = STAGES_A * BM * BK * 2 + STAGES * NB * BK * BN * 2;
+    // the bf16 epilogues stage a whole BM x (BN + 8) tile in the same LDS
+    static constexpr int STAGE_BF16 =
+        (MODE == kGateUp || MODE == kGateUpSave || MODE == kLinBf16) ? BM * (BN + 8) * 2 : 0;
+    static constexpr int SMEM = RING > STAGE_BF16 ? RING : STAGE_BF16;
 };
 
 // One tile (mt, nt), k-steps [k_begin, k_end) of BK, epilogue included. All

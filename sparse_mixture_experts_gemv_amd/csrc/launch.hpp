@@ -71,6 +71,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
 struct PlPlan {
     int bm, bn;                  // M tile rows, N tile columns (shared by the forward and input-gradient GEMMs)
     int n_mtiles, n_ntiles_fwd, n_ntiles_dx;
+    int bm_lin, n_mtiles_lin;    // M tiles of the grouped-output forward (bm_lin >= bm, so no more tiles)
     int wg_bm, wg_bn, wg_mt, wg_nt;  // weight-gradient tiles over [D_in, D_out]
     size_t tiles_off, order_off, counts_off, rows_off, xg_off, dyg_off, ws_bytes;
 };

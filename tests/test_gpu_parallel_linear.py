@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 MODES = [(False, False), (False, True), (True, False), (True, True)]
 SHAPES = [  # (S, k, D_in, D_out, E, skew)
+    (2000, 2, 128, 320, 4, None),  # 1000 rows per expert: 256-row tiles, D_out ragged
     (1000, 2, 128, 192, 4, None),  # 500 rows per expert: 192-row tiles
     (1000, 2, 128, 256, 8, None),  # 250: 128-row tiles
     (700, 2, 256, 320, 8, None),   # 175: 192-row tiles on the short-tile path; D_out ragged against 256 columns
@@ -118,7 +119,7 @@ def test_parallel_linear_bwd_partial_outputs_and_reproducible(oracle_lib):
     assert torch.equal(full[0], only_dx) and torch.equal(full[1], only_dw) and torch.equal(full[2], only_dg)
 
 
-@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[4], SHAPES[6]], ids=["128rows", "32rows_zipf", "empty_experts"])
+@pytest.mark.parametrize("shape", [SHAPES[2], SHAPES[5], SHAPES[7]], ids=["128rows", "32rows_zipf", "empty_experts"])
 def test_parallel_linear_bwd_bf16_dw(oracle_lib, shape):
     """moe_parallel_linear_bwd_bf16w: dw is the fp32 call's dw rounded to bf16 (RNE), bit for bit;
     dx and dgates are the fp32 call's; dw is also within the bar of the fp64 oracle."""
