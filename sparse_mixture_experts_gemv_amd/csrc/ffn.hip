@@ -266,9 +266,11 @@ static void launch_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t st
             case 256:
                 // short tiles skip missing rows where they are common; with
                 // ~1000 rows per expert the plain loop keeps the workgroups
-                // sharing a weight panel in step (half the HBM re-reads)
+                // sharing a weight panel in step (half the HBM re-reads), and
+                // its weight ring is 3 deep (two k-steps of weights in flight,
+                // the LDS full at 160 KB)
                 if (avg < 768) launch_pp_persistent<256, 128, MODE, 64, 2, 2, true>(p, stream);
-                else launch_pp_persistent<256, 128, MODE, 64, 2>(p, stream);
+                else launch_pp_persistent<256, 128, MODE, 64, 3, 2>(p, stream);
                 break;
             case 192: launch_pp_persistent<192, 128, MODE, 64, 3, 2, true>(p, stream); break;
             case 64: launch_pp_persistent<64, 128, MODE, 64, 3>(p, stream); break;

@@ -258,30 +258,34 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
 
     // ---- fragment read offsets within a stage ----
     const int fr = lane & 15, fg = lane >> 4;
-    int a_rd[KK][MT];
+    // The swizzles depend only on the low four bits of a row (A, B^T) or on
+    // bits 0, 1 and 3 of a k index (B), so offsets that differ by a multiple
+    // of 16 rows, or by 32 k and by 4 k, differ by a constant: one register
+    // per kk (A, B^T) or per j (B) and the rest as immediate offsets.
+    int a_rd[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KK; ++kk) {
+        const int row = wm * 16 + fr;
+        a_rd[kk] = row * A_ROW + (((kk * 4 + fg) ^ pp_a_swz<CH>(row)) << 4);
+    }
+    constexpr int A_RD_I = WM * 16 * A_ROW;  // + i * A_RD_I for block i
+    int b_rd[BT ? KK : NT];
+    if constexpr (BT) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int row = (WM * i + wm) * 16 + fr;
-            a_rd[kk][i] = row * A_ROW + (((kk * 4 + fg) ^ pp_a_swz<CH>(row)) << 4);
+        for (int kk = 0; kk < KK; ++kk) {
+            const int row = wn * WTN + fr;
+            b_rd[kk] = row * A_ROW + (((kk * 4 + fg) ^ pp_a_swz<CH>(row)) << 4);
         }
-    int b_rd[KK][NT][2];
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                if constexpr (BT) {  // one ds_read_b128 per operand, as for A
-                    const int row = wn * WTN + j * 16 + fr;
-                    b_rd[kk][j][h] = row * A_ROW + (((kk * 4 + fg) ^ pp_a_swz<CH>(row)) << 4);
-                } else {
-                    const int k = kk * 32 + 8 * fg + 4 * h + (fr >> 2);
-                    const int n = wn * WTN + j * 16 + 4 * (fr & 3);
-                    b_rd[kk][j][h] = k * B_ROW + (((n >> 4) ^ pp_b_swz<SEGS>(k)) << 5) + (n & 15) * 2;
-                }
-            }
+        for (int j = 0; j < NT; ++j) {
+            const int k = 8 * fg + (fr >> 2);
+            const int n = wn * WTN + j * 16 + 4 * (fr & 3);
+            b_rd[j] = k * B_ROW + (((n >> 4) ^ pp_b_swz<SEGS>(k)) << 5) + (n & 15) * 2;
+        }
+    }
+    // B^T: + j * B_RD_J for column block j; B: + kk * B_RD_KK + h * B_RD_H
+    constexpr int B_RD_J = 16 * A_ROW, B_RD_KK = 32 * B_ROW, B_RD_H = 4 * B_ROW;
 
     f32x4 acc[NB][MT][NT];
 #pragma unroll
@@ -317,21 +321,36 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
         }
         const char *sa = smem + SMOE_SLOT_A(kt) * A_BYTES;
         const char *sb = smem + B_RING + SMOE_SLOT_B(kt) * (NB * B_BYTES);
+        // one register per fragment column block holds slot base + lane
+        // offset; where there are many (kk, b, h) combinations per column
+        // block, the opaque move keeps the compiler from hoisting each into
+        // a register of its own, so the constants go into the reads' offset
+        // fields (with few, the hoisted form schedules better)
+        constexpr bool B_LANE_REG = !BT && KK * NB >= 4;
+        int b_lane[BT ? 1 : NT];
+        if constexpr (!BT) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                b_lane[j] = (int)(sb - smem) + b_rd[j];
+                if constexpr (B_LANE_REG) asm volatile("" : "+v"(b_lane[j]));
+            }
+        }
         uint4 af[KK][MT];
         uint4 bf[KK][NB][NT];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-            for (int i = 0; i < MT; ++i) af[kk][i] = *reinterpret_cast<const uint4 *>(sa + a_rd[kk][i]);
+            for (int i = 0; i < MT; ++i) af[kk][i] = *reinterpret_cast<const uint4 *>(sa + a_rd[kk] + i * A_RD_I);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     if constexpr (BT) {
-                        bf[kk][b][j] = *reinterpret_cast<const uint4 *>(sb + b * B_BYTES + b_rd[kk][j][0]);
+                        bf[kk][b][j] = *reinterpret_cast<const uint4 *>(sb + b * B_BYTES + b_rd[kk] + j * B_RD_J);
                     } else {
-                        const uint2 lo = pp_tr(sb + b * B_BYTES + b_rd[kk][j][0]);
-                        const uint2 hi = pp_tr(sb + b * B_BYTES + b_rd[kk][j][1]);
+                        const char *bp = smem + b_lane[j] + b * B_BYTES + kk * B_RD_KK;
+                        const uint2 lo = pp_tr(bp);
+                        const uint2 hi = pp_tr(bp + B_RD_H);
                         bf[kk][b][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
                     }
                 }
