@@ -279,7 +279,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
         q.n_mt = (F + 255) / 256;
         q.n_nt = (D + 255) / 256;
         prof_begin(stream, kKBwdWgrad);
-        grouped_wgrad_kernel<256, 256, 1, 32, 4><<<device_cus(), 512, 0, stream>>>(q);
+        launch_grouped_wgrad<256, 256, 1>(q, N, E, device_cus(), stream);
         prof_end(stream, kKBwdWgrad);
     }
     if (dw1 || dw3) {
@@ -301,7 +301,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
         if (!dw1) q.B0 = ab + F;   // only dw3: both halves compute x^T db
         if (!dw3) q.B1 = ab;       // only dw1: both halves compute x^T da
         prof_begin(stream, kKBwdWgrad);
-        grouped_wgrad_kernel<256, 128, 2, 32, 4><<<device_cus(), 512, 0, stream>>>(q);
+        launch_grouped_wgrad<256, 128, 2>(q, N, E, device_cus(), stream);
         prof_end(stream, kKBwdWgrad);
     }
 

@@ -351,7 +351,7 @@ hipError_t launch_pl_bwd(const uint16_t *x, const uint16_t *w, const float *gate
         q.n_mt = pl.wg_mt;
         q.n_nt = pl.wg_nt;
         prof_begin(stream, kKPlWgrad);
-        grouped_wgrad_kernel<256, 256, 1, 32, 4><<<device_cus(), 512, 0, stream>>>(q);
+        launch_grouped_wgrad<256, 256, 1>(q, N, E, device_cus(), stream);
         prof_end(stream, kKPlWgrad);
     }
     return hipGetLastError();
