@@ -134,10 +134,14 @@ static void bwd_tile(const GemmParams &p0, hipStream_t stream) {
         <<<device_cus(), 512, 0, stream>>>(p);
 }
 
-// gate+up recomputation: the tile shapes of the forward gate+up GEMM
-static void launch_recompute(int bm, const GemmParams &p, hipStream_t stream) {
+// gate+up recomputation: the tile shapes of the forward gate+up GEMM, with
+// its 3-deep weight ring from ~770 rows per expert
+static void launch_recompute(int bm, int64_t avg, const GemmParams &p, hipStream_t stream) {
     switch (bm) {
-        case 256: bwd_tile<256, 128, kGateUpSave, 64, 2, 2, false, 0>(p, stream); break;
+        case 256:
+            if (avg >= 768) bwd_tile<256, 128, kGateUpSave, 64, 3, 2, false, 0>(p, stream);
+            else bwd_tile<256, 128, kGateUpSave, 64, 2, 2, false, 0>(p, stream);
+            break;
         case 192: bwd_tile<192, 128, kGateUpSave, 64, 3, 2, true, 0>(p, stream); break;
         case 64: bwd_tile<64, 128, kGateUpSave, 64, 3, 3, false, 0>(p, stream); break;
         default: bwd_tile<32, 128, kGateUpSave, 64, 4, 4, false, 0>(p, stream); break;
@@ -224,7 +228,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
     p.K = D;
     if (!saved) {
         prof_begin(stream, kKBwdRecompute);
-        launch_recompute(pl.bm_r, p, stream);
+        launch_recompute(pl.bm_r, (int64_t)N / std::max(E, 1), p, stream);
         prof_end(stream, kKBwdRecompute);
     }
 
