@@ -174,8 +174,9 @@ PlPlan pl_plan(int64_t S, int64_t k, int64_t D_in, int64_t D_out, int64_t E) {
     pl.n_mtiles = tiles_upper_bound(N, E, pl.bm);
     // the grouped-output forward takes 256 x 256 tiles on experts of ~770
     // rows and more (Mixtral up-projection 1.02 -> 0.91 ms); the transposed
-    // input-gradient GEMM stays on the shared height (on 256 rows it is
-    // 60 % slower), so the tile table is built per launch
+    // input-gradient GEMM stays on the shared height (its 256-row instance
+    // reloads a spilled DMA offset inside the main loop and is 60 % slower),
+    // so the tile table is built per launch
     pl.bm_lin = avg >= 768 ? 256 : pl.bm;
     pl.n_mtiles_lin = tiles_upper_bound(N, E, pl.bm_lin);
     pl.n_ntiles_fwd = (int)((D_out + pl.bn - 1) / pl.bn);
