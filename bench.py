@@ -76,6 +76,74 @@ def roofline_entry(kernel: str, flops: float, nbytes: float, seconds: float, per
             f"algorithmic_flops_per_{per}": flops, f"avg_{per}_us": round(seconds * 1e6, 2)}
 
 
+def warm_up(step, n: int, min_seconds: float) -> int:
+    """At least `n` untimed steps and at least `min_seconds` of them: under sustained MFMA load the
+    GPU's clock settles over the first tens of milliseconds, and the timed steps should see the
+    steady state. Returns the number of steps run."""
+    import torch
+
+    done = 0
+    t0 = time.perf_counter()
+    while done < n or time.perf_counter() - t0 < min_seconds:
+        for _ in range(8 if done >= n else 1):
+            step()
+            done += 1
+        torch.cuda.synchronize()
+    return done
+
+
+def timed(step, steps: int, stream):
+    """ms per step over `steps` back-to-back steps, bracketed by HIP events on `stream`, plus the
+    wall-clock seconds of the region (synchronised on both sides)."""
+    import torch
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, time.perf_counter() - wall0
+
+
+def profiled(step, steps: int, stream):
+    """The same loop with per-kernel HIP-event pairs recorded around every launch (moe_profile_*):
+    {kernel: (total ms, launches)} and the ms per step of this loop."""
+    import sparse_mixture_experts_gemv_amd as smoe
+
+    smoe.profile_start(steps * 32)
+    ms, _ = timed(step, steps, stream)
+    return smoe.profile_stop(), ms
+
+
+def host_cpu_info() -> dict:
+    """What the CPU baseline ran on: the host's logical CPUs, the CPUs this process may use, the
+    threads the oracle is given (the CPU share of this process: OMP_NUM_THREADS when set, else the
+    affinity count) and the CPU model."""
+    nproc = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = nproc
+    share = affinity
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        share = min(share, int(env))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": nproc, "affinity": affinity, "threads": share, "model": model}
+
+
 def touched_experts(offsets) -> int:
     """Experts with at least one route, from the map's offsets (read back after timing)."""
     o = offsets.cpu()
@@ -104,7 +172,8 @@ def cpu_baseline(cfg, p, target_s: float = 15.0):
     import workloads as wl
 
     o = oracle.get()
-    nthreads = min(16, os.cpu_count() or 1)
+    host = host_cpu_info()
+    nthreads = host["threads"]
     rng = np.random.default_rng(0)
     order = rng.permutation(cfg.S)
     wg = wl.bf16_bits(p["wg"].cpu())
@@ -128,7 +197,8 @@ def cpu_baseline(cfg, p, target_s: float = 15.0):
         done += n
     return {"value": done / t_used, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{done} random tokens of the {cfg.name} workload (route + map + FFN, fp64, "
-                      f"{nthreads} threads, {t_used:.1f} s)"}
+                      f"{nthreads} threads, {t_used:.1f} s)",
+            "host": host}
 
 
 def pl_cpu_baseline(cfg, p, ids, gates, op, target_s: float = 15.0):
@@ -203,21 +273,9 @@ def bench_parallel_linear(args, cfg, p):
         flops = 4.0 * N * D * F  # dx and dw products (dgates is a by-product of the dx rows)
         dominant, dom_flops = None, 2.0 * N * D * F  # the slower of the dx and dw GEMMs
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    smoe.profile_start(args.steps * 16)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    kern = smoe.profile_stop()
-    ms = t0.elapsed_time(t1) / args.steps
+    warm_up(step, args.warmup, args.warmup_seconds)
+    ms, wall = timed(step, args.steps, stream)
+    kern, _ = profiled(step, args.steps, stream)
     if dominant is None:
         dominant = max(("pl_dx_gemm", "pl_wgrad_gemm"), key=lambda n: kern[n][0] / kern[n][1])
     dom_ms = kern[dominant][0] / kern[dominant][1]
@@ -317,21 +375,9 @@ def bench_ffn_bwd(args, cfg, p, train=False):
                   "bwd_wgrad_gemm": 6.0 * N * D * F, "bwd_dx_gemm": 4.0 * N * D * F,
                   "ffn_gate_up_gemm": 4.0 * N * D * F, "ffn_down_scatter_gemm": 2.0 * N * D * F}
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    smoe.profile_start(args.steps * 24)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    kern = smoe.profile_stop()
-    ms = t0.elapsed_time(t1) / args.steps
+    warm_up(step, args.warmup, args.warmup_seconds)
+    ms, wall = timed(step, args.steps, stream)
+    kern, _ = profiled(step, args.steps, stream)
     # the GEMM kind with the most time per step (the weight gradients run as two launches per step)
     per_step = {n: kern[n][0] / args.steps for n in gemm_flops if n in kern}
     dominant = max(per_step, key=per_step.get)
@@ -433,6 +479,10 @@ def main():
     ap.add_argument("--dw-bf16", action="store_true",
                     help="ffn_bwd / train / pl_bwd: weight gradients stored as bf16 (the *_bf16w entry points)")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the forward")
+    ap.add_argument("--no-combines", action="store_true",
+                    help="skip timing the forward with the atomic combine beside the default one")
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="warm-up runs at least this long as well as at least --warmup steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run three device-to-device copies of BYTES (HBM counter calibration)")
     args = ap.parse_args()
@@ -482,37 +532,37 @@ def main():
     topk = (p["ids"], p["weights"]) if "ids" in p else None
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
+    def step():
         layer.forward(p["x"], topk=topk)
-    torch.cuda.synchronize()
 
-    smoe.profile_start(args.steps * 16)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
-        layer.forward(p["x"], topk=topk)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    kern = smoe.profile_stop()
-    ms = t0.elapsed_time(t1) / args.steps
+    warm = warm_up(step, args.warmup, args.warmup_seconds)
+    # the headline: K steps with nothing but the forward passes in the stream
+    ms, wall = timed(step, args.steps, stream)
+    # per-kernel durations from a second loop of K steps with HIP events around every launch
+    kern, ms_profiled = profiled(step, args.steps, stream)
+
+    combines = None
+    if not args.no_combines:
+        # the other combine on the same inputs: the fp32 atomic scatter-add (smaller workspace)
+        alt = smoe.MoELayer(p["wg"], p["w1"], p["w3"], p["w2"], k, S, atomic=True)
+
+        def step_atomic():
+            alt.forward(p["x"], topk=topk)
+
+        warm_up(step_atomic, args.warmup, args.warmup_seconds)
+        ms_atomic, _ = timed(step_atomic, args.steps, stream)
+        kern_atomic, _ = profiled(step_atomic, args.steps, stream)
+        del alt
+        per = lambda kk: {n: round(1e3 * tot / c, 2) for n, (tot, c) in kk.items()}
+        combines = {"rows": {"ms_per_step": round(ms, 4), "kernels_us": per(kern)},
+                    "atomic": {"ms_per_step": round(ms_atomic, 4), "kernels_us": per(kern_atomic)}}
 
     graph_ms = None
     if not args.no_graph:
         # the same forward captured once as a HIP graph and replayed: no per-kernel launch cost
         layer.capture(p["x"], topk)
-        for _ in range(args.warmup):
-            layer.replay()
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for _ in range(args.steps):
-            layer.replay()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = t0.elapsed_time(t1) / args.steps
+        warm_up(layer.replay, args.warmup, args.warmup_seconds)
+        graph_ms, _ = timed(layer.replay, args.steps, stream)
 
     flops = layer_flops(S, D, F, E, k, with_router=topk is None)
     tokens_per_s = S / (ms / 1e3)
@@ -557,8 +607,12 @@ def main():
         "layer_mfma_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "kernels": {n: {"avg_us": round(v["avg_us"], 2), "launches": v["launches"]} for n, v in kernels.items()},
+        "ms_per_step_profiled_loop": round(ms_profiled, 4),
+        "warmup_steps_run": warm,
         "wall_s_timed_region": round(wall, 3),
     }
+    if combines is not None:
+        rec["combines"] = combines
     if graph_ms is not None:
         rec["graph_replay"] = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(S / (graph_ms / 1e3), 1)}
     if not args.no_cpu_baseline:

@@ -7,12 +7,14 @@
 // runs per tile and the result is scaled by the router coefficient and
 // accumulated into the token's output row.
 //
-// Launch sequence on one stream (no host synchronisation):
+// Launch sequence on one stream (no host synchronisation), default combine:
 //   tile_table  expert offsets -> (expert, row_begin, row_end) per M tile
-//   acc_zero    fp32 accumulator [S, D] = 0
 //   gate+up     h[r] = bf16(SiLU(x[t] W1[e]) * (x[t] W3[e]))  (gathered A)
-//   down        acc[t] += w_f * (h[r] W2[e])                  (fp32 atomics)
-//   finalize    out = bf16(acc)
+//   down        y[f] = w_f * (h[r] W2[e])        (fp32 row f of a per-route buffer)
+//   combine     out[t] = bf16(sum_j y[t k + j])   (j = 0 .. k-1 in order)
+// Atomic combine (smaller workspace): acc_zero (fp32 [S, D] = 0), gate+up,
+// down with acc[t] += w_f * (h[r] W2[e]) by fp32 atomics, finalize
+// out = bf16(acc).
 #include <algorithm>
 
 #include "gemm.hpp"

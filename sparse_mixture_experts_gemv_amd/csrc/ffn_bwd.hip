@@ -251,7 +251,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
     launch_bwd_bt<kSwigluBwd, kFlagBT>(pl.bm_b, (int64_t)N / E, p, stream);
     prof_end(stream, kKBwdDh);
 
-    if (dg) {
+    if (dg && N > 0) {  // S == 0 with a weight gradient requested reaches here: no routes, empty grid
         prof_begin(stream, kKBwdPrep);
         ffn_bwd_gate_reduce_kernel<<<(N + 63) / 64, 256, 0, stream>>>(part, pl.nparts, N, dg);
         prof_end(stream, kKBwdPrep);

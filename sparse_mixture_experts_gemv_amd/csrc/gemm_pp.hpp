@@ -1,8 +1,10 @@
 // Ping-pong grouped, gathered bf16 GEMM for gfx950 (MFMA 16x16x32).
 //
-// Contract as grouped_gemm_kernel (gemm.hpp). One workgroup of 8 waves (two
-// per SIMD) computes a BM x BN tile of one expert with one of the three
-// epilogues (fused SwiGLU gate+up, router-weighted scatter-add, fp32 store).
+// The GEMM contract and the epilogue modes (kGateUp, kDown, kDownRows,
+// kLogits, kLinBf16, kGateUpSave, kSwigluBwd) are described in gemm.hpp. One
+// workgroup of 8 waves (two per SIMD) computes a BM x BN tile of one expert
+// (pp_tile); the persistent and stream-K kernels at the end of this file walk
+// the tiles of a device-built block order.
 //
 // Operand path: HBM -> LDS by LDS DMA (buffer_load ... lds), A read back as
 // K-contiguous ds_read_b128 operands, B (weights, N-contiguous as stored)

@@ -4,7 +4,8 @@ Small shapes are compared element by element over every token; they cover
 each M-tile height the launcher picks (32, 64, 192, 256 rows), ragged N tiles
 (F or D not a multiple of 128), ragged M tails and empty experts. The five
 configurations run at their full sizes with the launch configuration of the
-benchmark, and sampled tokens are checked one by one against the oracle.
+benchmark, and every token is checked against the oracle (the tolerance bar
+is evaluated over all S*D outputs).
 Both combines are covered: the default per-route rows with an ordered sum
 (bitwise reproducible) and the fp32 atomic scatter-add (atomic=True)."""
 import numpy as np
@@ -12,7 +13,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import DEV, assert_close, make_problem, oracle_ffn_rows, sample_tokens, say
+from gpu_util import DEV, assert_close, make_problem, oracle_ffn_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -136,7 +137,16 @@ def test_ffn_rows_combine_is_bitwise_reproducible(S):
     assert np.array_equal(a, b)
 
 
-def full_layer(oracle_lib, cfg, S=None, n_sample=24, atomic=False):
+# Oracle references of the full-size layers, keyed by (configuration, S). The
+# router is deterministic, so the atomic-combine run of a configuration sees
+# the same ids as its rows run and reuses the reference (checked: ids equal).
+_FULL_REFS = {}
+
+
+def full_layer(oracle_lib, cfg, S=None, atomic=False):
+    """The whole forward (route, map, FFN, combine) at full size in the benchmark's launch
+    configuration, compared with the fp64 oracle on EVERY token: MAE and max-rel are taken over
+    all S*D outputs, the map is compared bit for bit."""
     import sparse_mixture_experts_gemv_amd as smoe
     p = make_problem(cfg, S=S)
     S = p["S"]
@@ -144,41 +154,53 @@ def full_layer(oracle_lib, cfg, S=None, n_sample=24, atomic=False):
     topk = (p["ids"], p["weights"]) if "ids" in p else None
     out = layer.forward(p["x"], topk=topk)
     torch.cuda.synchronize()
-    out2 = layer.forward(p["x"], topk=topk)  # repeat: same bits (ordered combine) or fp32 atomics jitter
+    out2 = layer.forward(p["x"], topk=topk)
     torch.cuda.synchronize()
     ids = (p["ids"] if topk else layer.ids).cpu().numpy()
     got = out.float().cpu().numpy().astype(np.float64)
-    tokens = sample_tokens(S, n_sample, seed=cfg.cfg_id + S)
-    if topk:
-        weights = p["weights"].cpu().numpy().astype(np.float64)
-    else:  # oracle conditioned on the GPU's ids: fp64 softmax over those experts' logits
-        _, weights_t, _ = oracle_lib.route(wl.bf16_bits(p["x"][torch.from_numpy(tokens).to(DEV)].cpu()),
-                                           wl.bf16_bits(p["wg"].cpu()), cfg.k, ids_in=ids[tokens])
-        weights = np.zeros((S, cfg.k))
-        weights[tokens] = weights_t
     # the map of the full run is bit-exact against the oracle's
     smap = [t.cpu().numpy() for t in layer.map]
     ref_map = oracle_lib.sparse_map(ids, cfg.E)
     for g, r in zip(smap, ref_map):
         assert np.array_equal(g, r)
-    ref = oracle_ffn_rows(oracle_lib, p, ids, weights, tokens)
-    m = assert_close(got[tokens], ref, f"{cfg.name} S={S} ({len(tokens)} sampled tokens, "
-                                       f"{'atomic' if atomic else 'rows'})")
-    d = np.abs(out2.float().cpu().numpy() - got).max()
-    assert d <= (2e-2 if atomic and cfg.k > 2 else 0), d
+    key = (cfg.name, S)
+    cached = _FULL_REFS.get(key)
+    if cached is not None and np.array_equal(cached[0], ids):
+        ref = cached[1]
+    else:
+        if topk:
+            weights = p["weights"].cpu().numpy().astype(np.float64)
+        else:  # oracle conditioned on the GPU's ids: fp64 softmax over those experts' logits
+            _, weights, _ = oracle_lib.route(wl.bf16_bits(p["x"].cpu()), wl.bf16_bits(p["wg"].cpu()), cfg.k,
+                                             ids_in=ids)
+        say(f"  oracle: all {S} tokens of {cfg.name}")
+        ref = oracle_ffn_rows(oracle_lib, p, ids, weights, np.arange(S))
+        _FULL_REFS[key] = (ids, ref)
+    m = assert_close(got, ref, f"{cfg.name} S={S} (all {S} tokens, {S * cfg.D} outputs, "
+                               f"{'atomic' if atomic else 'rows'})")
+    again = out2.float().cpu().numpy().astype(np.float64)
+    if atomic:
+        # fp32 atomics add the k routes in arrival order: a repeat may differ in the last bits,
+        # and is held to the same bar against the oracle
+        assert_close(again, ref, f"{cfg.name} S={S} repeat (atomic)")
+    else:
+        assert np.array_equal(again, got)  # the ordered combine repeats bit for bit
     return m
 
 
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("atomic", [False, True], ids=["rows", "atomic"])
 @pytest.mark.parametrize("name", ["tiny", "mixtral", "gptoss", "dsv3"])
 def test_layer_full_size(oracle_lib, name, atomic):
     cfg = wl.CONFIGS[name]
     say(f"layer {cfg.describe()}")
-    full_layer(oracle_lib, cfg, n_sample=cfg.S if name == "tiny" else 24, atomic=atomic)
+    full_layer(oracle_lib, cfg, atomic=atomic)
 
 
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("atomic", [False, True], ids=["rows", "atomic"])
 @pytest.mark.parametrize("S", wl.QWEN2_BATCHES)
-def test_layer_qwen2_zipf(oracle_lib, S):
+def test_layer_qwen2_zipf(oracle_lib, S, atomic):
     cfg = wl.CONFIGS["qwen2"]
     say(f"layer {cfg.with_S(S).describe()}")
-    full_layer(oracle_lib, cfg, S=S, n_sample=min(S, 24), atomic=(S == 512))
+    full_layer(oracle_lib, cfg, S=S, atomic=atomic)

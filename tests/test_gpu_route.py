@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import DEV, host_bits, near_tie_tokens, sample_tokens, say
+from gpu_util import DEV, host_bits, near_tie_tokens, say
 
 pytestmark = pytest.mark.gpu
 
@@ -41,13 +41,13 @@ def check_route(o, x, wg, k, what, tokens=None):
     assert np.allclose(w.sum(1), 1.0, atol=1e-5)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["tiny", "mixtral", "gptoss", "dsv3"])
 def test_route_configs(oracle_lib, name):
     cfg = wl.CONFIGS[name]
     x = wl.gen_x(cfg).to(DEV)
     wg = wl.gen_w_gate(cfg).to(DEV)
-    tokens = sample_tokens(cfg.S, 512, seed=cfg.cfg_id)
-    check_route(oracle_lib, x, wg, cfg.k, name, tokens)
+    check_route(oracle_lib, x, wg, cfg.k, name)  # every token
 
 
 @pytest.mark.parametrize("S,D,E,k", [(1, 64, 8, 1), (37, 128, 16, 3), (300, 192, 64, 8), (129, 256, 256, 16),
