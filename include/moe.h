@@ -67,7 +67,8 @@ typedef enum {
     MOE_ERR_INVALID_ARGUMENT = 1,
     MOE_ERR_UNSUPPORTED = 2,
     MOE_ERR_WORKSPACE_TOO_SMALL = 3,
-    MOE_ERR_LAUNCH = 4
+    MOE_ERR_LAUNCH = 4,
+    MOE_ERR_SCRATCH_LIMIT = 5 /* a no-allocation call needs more than its static scratch holds */
 } moe_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -125,6 +126,30 @@ size_t moe_sparse_map_workspace_bytes(int32_t S, int32_t k, int32_t E);
 int moe_sparse_map(const int32_t *topk_ids, int32_t S, int32_t k, int32_t E, int32_t *expert_counts,
                    int32_t *expert_offsets, int32_t *sparse_rows, int32_t *slot_src, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/*
+ * moe_sparse_map without a workspace argument, for callers that cannot
+ * allocate device memory (code being captured into a HIP graph, serving loops
+ * that forbid hipMalloc, harnesses without an allocator). It runs the same
+ * kernels and gives the same outputs, bit for bit, as moe_sparse_map; the
+ * per-chunk count matrix that moe_sparse_map keeps in its workspace lives here
+ * in a static device array of the library instead: 4 MiB + 4 KiB per GPU,
+ * reserved in each GPU's memory when the library's code is loaded there and
+ * held until the process ends. The call itself allocates nothing.
+ *  - That scratch covers every map with E <= 512 and, for 512 < E <= 1024,
+ *    maps of up to about 2.6e5 routes; a map that needs more returns
+ *    MOE_ERR_SCRATCH_LIMIT before anything is enqueued (moe_sparse_map with a
+ *    workspace of moe_sparse_map_workspace_bytes() serves those).
+ *  - Every call on one GPU uses that GPU's single copy of the scratch, and the
+ *    kernels write every count they read, so no clearing is needed between
+ *    calls. Calls that overlap in time on one GPU (for example on two
+ *    streams) race on the scratch and give undefined results: serialise them.
+ *  - The first call on a device looks up the scratch's device address (with
+ *    that device current); a failure there returns MOE_ERR_LAUNCH.
+ * Arguments, outputs, limits and the other errors as moe_sparse_map.
+ */
+int moe_sparse_map_noalloc(const int32_t *topk_ids, int32_t S, int32_t k, int32_t E, int32_t *expert_counts,
+                           int32_t *expert_offsets, int32_t *sparse_rows, int32_t *slot_src, void *stream);
 
 /*
  * Workspace bytes for the default combine of moe_scatter_ffn_fwd: the

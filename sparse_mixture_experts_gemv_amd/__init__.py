@@ -13,11 +13,12 @@ kernels behind a C ABI (include/moe.h), called through a thin ctypes binding.
 """
 from ._lib import (MoEError, MoELayer, layer_fwd, load, profile_start, profile_stop, moe_parallel_linear_bwd,
                    moe_parallel_linear_fwd, moe_route_topk, moe_scatter_ffn_bwd, moe_scatter_ffn_fwd, moe_sparse_map,
+                   moe_sparse_map_noalloc,
                    parallel_linear_workspace_bytes, route_workspace_bytes, saved_activations_numel,
                    scatter_ffn_bwd_workspace_bytes, scatter_ffn_workspace_bytes, sparse_map_workspace_bytes, status_str)
 
 __all__ = ["MoEError", "MoELayer", "layer_fwd", "load", "profile_start", "profile_stop", "moe_parallel_linear_bwd",
            "moe_parallel_linear_fwd", "moe_route_topk", "moe_scatter_ffn_bwd", "moe_scatter_ffn_fwd", "moe_sparse_map",
-           "parallel_linear_workspace_bytes", "route_workspace_bytes", "saved_activations_numel",
+           "moe_sparse_map_noalloc", "parallel_linear_workspace_bytes", "route_workspace_bytes", "saved_activations_numel",
            "scatter_ffn_bwd_workspace_bytes",
            "scatter_ffn_workspace_bytes", "sparse_map_workspace_bytes", "status_str"]

@@ -27,6 +27,7 @@ SIGNATURES = {
     "moe_route_topk": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "moe_sparse_map_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "moe_sparse_map": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_sparse_map_noalloc": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_scatter_ffn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_scatter_ffn_workspace_bytes_atomic": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_scatter_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ,
@@ -177,6 +178,21 @@ def moe_sparse_map(topk_ids: torch.Tensor, E: int, out: Optional[Tuple[torch.Ten
     _check(load().moe_sparse_map(_ptr(topk_ids), S, k, E, _ptr(counts), _ptr(offsets), _ptr(rows), _ptr(src),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_sparse_map")
     return counts, offsets, rows, src
+
+
+def moe_sparse_map_noalloc(topk_ids: torch.Tensor, E: int, out: Tuple[torch.Tensor, ...], stream=None):
+    """moe_sparse_map on the library's static per-GPU scratch (no workspace, nothing allocated by the
+    call): fills out = (expert_counts [E], expert_offsets [E+1], sparse_rows [S*k], slot_src [S*k])."""
+    S, k = topk_ids.shape
+    _dev(topk_ids, torch.int32, "topk_ids")
+    counts, offsets, rows, src = out
+    _dev(counts, torch.int32, "expert_counts", (E,))
+    _dev(offsets, torch.int32, "expert_offsets", (E + 1,))
+    _dev(rows, torch.int32, "sparse_rows", (S * k,))
+    _dev(src, torch.int32, "slot_src", (S * k,))
+    _check(load().moe_sparse_map_noalloc(_ptr(topk_ids), S, k, E, _ptr(counts), _ptr(offsets), _ptr(rows),
+                                         _ptr(src), _stream(stream)), "moe_sparse_map_noalloc")
+    return out
 
 
 def moe_scatter_ffn_fwd(x: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,

@@ -21,6 +21,7 @@ const char *moe_status_str(int status) {
         case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
         case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
         case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH";
+        case MOE_ERR_SCRATCH_LIMIT: return "MOE_ERR_SCRATCH_LIMIT";
         default: return "MOE_ERR_UNKNOWN";
     }
 }
@@ -69,6 +70,27 @@ int moe_sparse_map(const int32_t *topk_ids, int32_t S, int32_t k, int32_t E, int
     }
     return finish(smoe::launch_sparse_map(topk_ids, (int)N, E, expert_counts, expert_offsets, sparse_rows, slot_src,
                                           workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int moe_sparse_map_noalloc(const int32_t *topk_ids, int32_t S, int32_t k, int32_t E, int32_t *expert_counts,
+                           int32_t *expert_offsets, int32_t *sparse_rows, int32_t *slot_src, void *stream) {
+    if (S < 0 || k < 1 || E < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+    if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARGUMENT;
+    if (misaligned(expert_counts) || misaligned(expert_offsets)) return MOE_ERR_INVALID_ARGUMENT;
+    if (E > 1024) return MOE_ERR_UNSUPPORTED;
+    const int64_t N = (int64_t)S * k;
+    if (N >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    void *scratch = nullptr;
+    if (N > 0) {
+        if (!topk_ids || !sparse_rows || !slot_src) return MOE_ERR_INVALID_ARGUMENT;
+        if (misaligned(topk_ids) || misaligned(sparse_rows) || misaligned(slot_src)) return MOE_ERR_INVALID_ARGUMENT;
+        if (smoe::sparse_map_plan(N, E).ws_bytes > smoe::kSparseMapNoallocScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+        // this GPU's copy of the library's static scratch (no allocation; looked up once per device)
+        if (smoe::sparse_map_noalloc_scratch(&scratch) != hipSuccess) return MOE_ERR_LAUNCH;
+    }
+    // the kernels write every count they later read: the scratch needs no clearing
+    return finish(smoe::launch_sparse_map(topk_ids, (int)N, E, expert_counts, expert_offsets, sparse_rows, slot_src,
+                                          scratch, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t moe_scatter_ffn_workspace_bytes(int32_t S, int32_t D, int32_t F, int32_t E, int32_t k) {

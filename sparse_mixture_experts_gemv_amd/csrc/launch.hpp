@@ -19,6 +19,12 @@ struct SparseMapPlan {
     size_t ws_bytes;
 };
 SparseMapPlan sparse_map_plan(int64_t N, int E);
+// Static per-GPU scratch of moe_sparse_map_noalloc: enough for every map with
+// E <= 512 (the plan's count matrix holds at most max(2048, 2^20 / E) columns
+// of E counts, plus E totals).
+constexpr size_t kSparseMapNoallocScratchBytes = (size_t)4 << 20 | (size_t)4 << 10;
+// Device address of this GPU's copy of that scratch (looked up once per device).
+hipError_t sparse_map_noalloc_scratch(void **ptr);
 hipError_t launch_sparse_map(const int32_t *ids, int N, int E, int32_t *expert_counts, int32_t *expert_offsets,
                              int32_t *sparse_rows, int32_t *slot_src, void *workspace, hipStream_t stream);
 

@@ -21,6 +21,7 @@
 //   pass 2 (rowscan): per expert, exclusive scan over sub-chunks, total
 //   pass 3 (assign):  offsets from the totals, then rank -> slot
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -317,6 +318,37 @@ SparseMapPlan sparse_map_plan(int64_t N, int E) {
     pl.nbits = 32 - __builtin_clz((unsigned)E);  // bits to hold 0..E (E is the sentinel)
     pl.ws_bytes = (size_t)E * (size_t)pl.nsub * sizeof(int32_t) + (size_t)E * sizeof(int32_t);
     return pl;
+}
+
+// ---- no-allocation form ----
+// Scratch of the no-allocation entry point: one copy per GPU in the code
+// object's static device memory, held until the process ends. Host code never
+// uses this name as an address (on the host it is only a stand-in for the
+// symbol): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) char scratch[kSparseMapNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t sparse_map_noalloc_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_sparse_map(const int32_t *ids, int N, int E, int32_t *expert_counts, int32_t *expert_offsets,

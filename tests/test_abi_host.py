@@ -28,7 +28,7 @@ def header_functions():
 def test_exports_every_declared_symbol(lib):
     import sparse_mixture_experts_gemv_amd._lib as b
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.SIGNATURES)
@@ -41,6 +41,7 @@ def test_status_strings(lib):
     assert smoe.status_str(2) == "MOE_ERR_UNSUPPORTED"
     assert smoe.status_str(3) == "MOE_ERR_WORKSPACE_TOO_SMALL"
     assert smoe.status_str(4) == "MOE_ERR_LAUNCH"
+    assert smoe.status_str(5) == "MOE_ERR_SCRATCH_LIMIT"
     assert smoe.status_str(99) == "MOE_ERR_UNKNOWN"
     assert lib.moe_version() >= 100
 
