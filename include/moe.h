@@ -136,10 +136,12 @@ int moe_sparse_map(const int32_t *topk_ids, int32_t S, int32_t k, int32_t E, int
  * in a static device array of the library instead: 4 MiB + 4 KiB per GPU,
  * reserved in each GPU's memory when the library's code is loaded there and
  * held until the process ends. The call itself allocates nothing.
- *  - That scratch covers every map with E <= 512 and, for 512 < E <= 1024,
- *    maps of up to about 2.6e5 routes; a map that needs more returns
- *    MOE_ERR_SCRATCH_LIMIT before anything is enqueued (moe_sparse_map with a
- *    workspace of moe_sparse_map_workspace_bytes() serves those).
+ *  - That scratch serves exactly the maps whose
+ *    moe_sparse_map_workspace_bytes() is at most its size: every map with
+ *    E <= 512, every map of fewer than 2^20 routes, and at E = 1024 maps of
+ *    up to 2^22 routes. A map that needs more returns MOE_ERR_SCRATCH_LIMIT
+ *    before anything is enqueued (moe_sparse_map with a workspace of
+ *    moe_sparse_map_workspace_bytes() serves those).
  *  - Every call on one GPU uses that GPU's single copy of the scratch, and the
  *    kernels write every count they read, so no clearing is needed between
  *    calls. Calls that overlap in time on one GPU (for example on two

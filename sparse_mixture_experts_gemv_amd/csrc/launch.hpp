@@ -13,8 +13,9 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // ---- sparse map ----
 struct SparseMapPlan {
-    int L;        // routes per wavefront sub-chunk
-    int nsub;     // number of sub-chunks
+    int L;        // routes per chunk (one workgroup of the multi-pass form)
+    int nsub;     // number of chunks
+    int rg;       // groups of 64 routes per wave and round (1 or 4)
     int nbits;    // id bits examined by match-any (covers the sentinel E)
     size_t ws_bytes;
 };

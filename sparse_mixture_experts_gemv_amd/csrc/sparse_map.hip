@@ -11,15 +11,16 @@
 // Unlike that pull request's atomic slot claim, the assignment here is a
 // stable rank, so the map is identical on every run.
 //
-// Layout of the work: the routes are cut into sub-chunks of L routes, one
-// per wavefront, processed 64 at a time. Within a group of 64, a lane finds
-// the lanes holding the same expert with one ballot per id bit (match-any),
-// so its rank among them is a popcount and the group's count per expert is
-// known to the lowest such lane, which updates a per-wave LDS counter. No
-// global atomics are used anywhere.
-//   pass 1 (hist):    per sub-chunk counts  -> cnt[e][sub]       (workspace)
-//   pass 2 (rowscan): per expert, exclusive scan over sub-chunks, total
-//   pass 3 (assign):  offsets from the totals, then rank -> slot
+// Layout of the work: routes are taken 64 at a time by a wavefront. Within a
+// group of 64, a lane finds the lanes holding the same expert with one ballot
+// per id bit (match-any), so its rank among them is a popcount and the
+// group's count per expert is known to the lowest such lane, which updates a
+// per-wave LDS counter. No global atomics are used anywhere. Large maps:
+//   pass 1 (hist):    per chunk of routes, counts -> cnt[e][chunk] (workspace)
+//   pass 2 (rowscan): per expert, exclusive scan over chunks, total
+//   pass 3 (assign):  offsets from the totals, then per chunk a local stable
+//                     sort by expert in LDS -> slots, written out in runs
+// Small maps (at most 8192 routes) take all three steps in one workgroup.
 #include <algorithm>
 #include <mutex>
 
@@ -29,9 +30,8 @@
 
 namespace smoe {
 
-constexpr int kMapWaves = 4;
 constexpr int kMaxExperts = 1024;
-constexpr int kMapUnroll = 4;  // groups of 64 routes whose ids are loaded together
+constexpr int kMapUnroll = 4;  // groups of 64 routes whose ids are loaded together (small maps)
 
 __device__ __forceinline__ unsigned long long match_any(int key, int nbits) {
     unsigned long long m = __ballot(1);
@@ -41,36 +41,6 @@ __device__ __forceinline__ unsigned long long match_any(int key, int nbits) {
         m &= bit ? bb : ~bb;
     }
     return m;
-}
-
-__global__ __launch_bounds__(256) void smap_hist_kernel(const int32_t *__restrict__ ids, int N, int E, int nbits,
-                                                         int L, int nsub, int32_t *__restrict__ cnt) {
-    __shared__ int32_t s_cnt[kMapWaves * kMaxExperts];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int sub = blockIdx.x * kMapWaves + w;
-    int32_t *my = s_cnt + w * E;
-    for (int e = lane; e < E; e += 64) my[e] = 0;
-    __syncthreads();
-    if (sub < nsub) {
-        const int base = sub * L;
-        for (int g0 = 0; g0 < L; g0 += 64 * kMapUnroll) {
-            int ev[kMapUnroll];  // the ids of kMapUnroll groups are loaded before any is used
-#pragma unroll
-            for (int u = 0; u < kMapUnroll; ++u) {
-                const int f = base + g0 + 64 * u + lane;
-                ev[u] = f < N ? ids[f] : E;  // E = sentinel: lanes past the end, ids outside [0, E)
-            }
-#pragma unroll
-            for (int u = 0; u < kMapUnroll; ++u) {
-                int e = ev[u];
-                if ((unsigned)e >= (unsigned)E) e = E;
-                const unsigned long long m = match_any(e, nbits);
-                const int leader = __ffsll(m) - 1;
-                if (lane == leader && e < E) my[e] += __popcll(m);
-            }
-        }
-        for (int e = lane; e < E; e += 64) cnt[(size_t)e * nsub + sub] = my[e];
-    }
 }
 
 // Block-wide exclusive scan of one int per thread (256 threads); returns the
@@ -121,79 +91,6 @@ __global__ __launch_bounds__(256) void smap_rowscan_kernel(int32_t *__restrict__
         running += tot;
     }
     if (threadIdx.x == 0) totals[e] = running;
-}
-
-__global__ __launch_bounds__(256) void smap_assign_kernel(const int32_t *__restrict__ ids, int N, int E, int nbits,
-                                                           int L, int nsub, const int32_t *__restrict__ cnt,
-                                                           const int32_t *__restrict__ totals,
-                                                           int32_t *__restrict__ expert_counts,
-                                                           int32_t *__restrict__ expert_offsets,
-                                                           int32_t *__restrict__ sparse_rows,
-                                                           int32_t *__restrict__ slot_src) {
-    __shared__ int32_t s_off[kMaxExperts];
-    __shared__ int32_t s_ctr[kMapWaves * kMaxExperts];
-    __shared__ int s_tmp[4];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-
-    // offsets = exclusive scan of the per-expert totals (E <= 1024: 4 per thread)
-    {
-        int v[4], s = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = threadIdx.x * 4 + i;
-            v[i] = e < E ? totals[e] : 0;
-            s += v[i];
-        }
-        int tot;
-        int pre = block_exscan_256(s, s_tmp, &tot);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = threadIdx.x * 4 + i;
-            if (e < E) {
-                s_off[e] = pre;
-                if (blockIdx.x == 0) {
-                    expert_counts[e] = v[i];
-                    expert_offsets[e] = pre;
-                }
-            }
-            pre += v[i];
-        }
-        if (blockIdx.x == 0 && threadIdx.x == 0) expert_offsets[E] = tot;
-    }
-    __syncthreads();
-
-    const int sub = blockIdx.x * kMapWaves + w;
-    if (sub >= nsub) return;
-    int32_t *my = s_ctr + w * E;
-    for (int e = lane; e < E; e += 64) my[e] = s_off[e] + cnt[(size_t)e * nsub + sub];
-    const int base = sub * L;
-    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int g0 = 0; g0 < L; g0 += 64 * kMapUnroll) {
-        int ev[kMapUnroll];
-#pragma unroll
-        for (int u = 0; u < kMapUnroll; ++u) {
-            const int f = base + g0 + 64 * u + lane;
-            ev[u] = f < N ? ids[f] : E;
-        }
-#pragma unroll
-        for (int u = 0; u < kMapUnroll; ++u) {
-            const int f = base + g0 + 64 * u + lane;
-            int e = ev[u];
-            if ((unsigned)e >= (unsigned)E) e = E;
-            const unsigned long long m = match_any(e, nbits);
-            const int leader = __ffsll(m) - 1;
-            int b = (lane == leader && e < E) ? my[e] : 0;
-            b = __shfl(b, leader);
-            if (e < E) {
-                const int slot = b + __popcll(m & lt);
-                sparse_rows[f] = slot;
-                slot_src[slot] = f;
-            } else if (f < N) {
-                sparse_rows[f] = -1;  // id outside [0, E): the route gets no slot
-            }
-            if (lane == leader && e < E) my[e] = b + __popcll(m);
-        }
-    }
 }
 
 // The whole map in one workgroup of 1024 threads, for maps of at most
@@ -297,6 +194,179 @@ __global__ __launch_bounds__(1024) void smap_small_kernel(const int32_t *__restr
     }
 }
 
+// ---- large maps: chunks of routes per 1024-thread workgroup ----
+//
+// The routes are cut into chunks of C consecutive routes, one per workgroup,
+// walked in rounds of 16 waves x RG groups of 64 routes. The histogram pass
+// counts each chunk's routes per expert (cnt[e][chunk]); after the row scan
+// over chunks, the assignment pass takes each round of its chunk, ranks the
+// round's routes stably by expert in LDS (per-wave counts from match-any,
+// their prefix over the waves, and the prefix over experts), writes
+// sparse_rows in route order and then slot_src from the locally sorted
+// order: the routes of one expert in one round have consecutive slots, so
+// slot_src leaves as runs of consecutive 4-byte words instead of one
+// scattered word per lane. The slots are those of the stable sort, as in
+// every other form of the map.
+constexpr int kBigWaves = 16;
+
+// Exclusive scan of one int per thread over a 1024-thread workgroup; returns
+// the thread's exclusive prefix and the total in *total.
+__device__ int block_exscan_1024(int v, int *s_tmp, int *total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kBigWaves; ++i) {
+        if (i < w) base += s_tmp[i];
+        tot += s_tmp[i];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + x - v;
+}
+
+template <int RG>
+__global__ __launch_bounds__(1024) void smap_chunk_hist_kernel(const int32_t *__restrict__ ids, int N, int E, int nbits,
+                                                               int C, int nchunks, int32_t *__restrict__ cnt) {
+    extern __shared__ int32_t s_cnt[];  // [wave][expert], 16 E ints
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int32_t *my = s_cnt + w * E;
+    for (int e = lane; e < E; e += 64) my[e] = 0;
+    const int base = blockIdx.x * C;
+    const int end = min(N, base + C);
+    constexpr int ROUND = kBigWaves * 64 * RG;
+    for (int r0 = base; r0 < end; r0 += ROUND) {
+        int ev[RG];
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            const int f = r0 + (w * RG + u) * 64 + lane;
+            ev[u] = f < end ? ids[f] : E;
+        }
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            int e = ev[u];
+            if ((unsigned)e >= (unsigned)E) e = E;
+            const unsigned long long m = match_any(e, nbits);
+            if (lane == __ffsll(m) - 1 && e < E) my[e] += __popcll(m);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 1024) {
+        int t = 0;
+        for (int i = 0; i < kBigWaves; ++i) t += s_cnt[i * E + e];
+        cnt[(size_t)e * nchunks + blockIdx.x] = t;
+    }
+}
+
+constexpr size_t chunk_hist_lds_bytes(int E) { return (size_t)kBigWaves * E * sizeof(int32_t); }
+constexpr size_t chunk_assign_lds_bytes(int E, int RG) {
+    return (size_t)(kBigWaves + 2) * E * sizeof(int32_t) + (size_t)kBigWaves * 64 * RG * (sizeof(int32_t) + sizeof(int16_t));
+}
+
+template <int RG>
+__global__ __launch_bounds__(1024) void smap_chunk_assign_kernel(
+    const int32_t *__restrict__ ids, int N, int E, int nbits, int C, int nchunks, const int32_t *__restrict__ cnt,
+    const int32_t *__restrict__ totals, int32_t *__restrict__ expert_counts, int32_t *__restrict__ expert_offsets,
+    int32_t *__restrict__ sparse_rows, int32_t *__restrict__ slot_src) {
+    constexpr int ROUND = kBigWaves * 64 * RG;
+    // LDS (chunk_assign_lds_bytes): s_wc [16][E] per-wave counts of the round,
+    // then the waves' starts; s_base [E] next slot of expert e in this chunk;
+    // s_lofs [E] start of expert e's run in the round's local order; s_f
+    // [ROUND] the round's routes sorted by expert; s_e [ROUND] their experts
+    extern __shared__ int32_t s_lds[];
+    int32_t *s_wc = s_lds;
+    int32_t *s_base = s_wc + kBigWaves * E;
+    int32_t *s_lofs = s_base + E;
+    int32_t *s_f = s_lofs + E;
+    int16_t *s_e = reinterpret_cast<int16_t *>(s_f + ROUND);
+    __shared__ int s_tmp[kBigWaves];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    // offsets = exclusive scan of the per-expert totals (thread e owns expert e, E <= 1024)
+    {
+        const int e = tid;
+        const int v = e < E ? totals[e] : 0;
+        int tot;
+        const int off = block_exscan_1024(v, s_tmp, &tot);
+        if (e < E) {
+            s_base[e] = off + cnt[(size_t)e * nchunks + blockIdx.x];  // cnt holds the scan over chunks
+            if (blockIdx.x == 0) {
+                expert_counts[e] = v;
+                expert_offsets[e] = off;
+            }
+        }
+        if (blockIdx.x == 0 && e == 0) expert_offsets[E] = tot;
+    }
+    int32_t *my = s_wc + w * E;
+    const int base = blockIdx.x * C;
+    const int end = min(N, base + C);
+    for (int r0 = base; r0 < end; r0 += ROUND) {
+        for (int e = lane; e < E; e += 64) my[e] = 0;
+        // ranks within the wave (groups in order, lanes in order)
+        int ev[RG], rk[RG];
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            const int f = r0 + (w * RG + u) * 64 + lane;
+            ev[u] = f < end ? ids[f] : E;
+        }
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            int e = ev[u];
+            if ((unsigned)e >= (unsigned)E) e = E;
+            ev[u] = e;
+            const unsigned long long m = match_any(e, nbits);
+            const int leader = __ffsll(m) - 1;
+            int b = (lane == leader && e < E) ? my[e] : 0;
+            b = __shfl(b, leader);
+            rk[u] = b + __popcll(m & lt);
+            if (lane == leader && e < E) my[e] = b + __popcll(m);
+        }
+        __syncthreads();
+        // thread e: the waves' starts within expert e's run, and the run starts (scan over experts)
+        int tot_e = 0;
+        if (tid < E)
+            for (int i = 0; i < kBigWaves; ++i) {
+                const int c = s_wc[i * E + tid];
+                s_wc[i * E + tid] = tot_e;
+                tot_e += c;
+            }
+        int round_total;
+        const int lofs = block_exscan_1024(tid < E ? tot_e : 0, s_tmp, &round_total);
+        if (tid < E) s_lofs[tid] = lofs;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            const int f = r0 + (w * RG + u) * 64 + lane;
+            const int e = ev[u];
+            if (e < E) {
+                const int lpos = s_lofs[e] + s_wc[w * E + e] + rk[u];
+                s_f[lpos] = f;
+                s_e[lpos] = (int16_t)e;
+                sparse_rows[f] = s_base[e] + (lpos - s_lofs[e]);
+            } else if (f < end) {
+                sparse_rows[f] = -1;  // id outside [0, E): the route gets no slot
+            }
+        }
+        __syncthreads();
+        // slot_src from the local order: consecutive positions of one expert are consecutive slots
+        for (int q = tid; q < round_total; q += 1024) {
+            const int e = s_e[q];
+            slot_src[s_base[e] + (q - s_lofs[e])] = s_f[q];
+        }
+        __syncthreads();
+        if (tid < E) s_base[tid] += tot_e;
+        __syncthreads();
+    }
+}
+
 __global__ void smap_empty_kernel(int E, int32_t *expert_counts, int32_t *expert_offsets) {
     for (int e = threadIdx.x; e <= E; e += blockDim.x) {
         if (e < E) expert_counts[e] = 0;
@@ -306,15 +376,16 @@ __global__ void smap_empty_kernel(int E, int32_t *expert_counts, int32_t *expert
 
 SparseMapPlan sparse_map_plan(int64_t N, int E) {
     SparseMapPlan pl;
-    // sub-chunks of L = 256 * 2^j routes (a multiple of 64 * kMapUnroll); up
-    // to max(2048, 2^20 / E) of them, so large maps keep many waves busy (a
-    // wave's loop over its L routes is latency-bound) while the per-sub-chunk
-    // count matrix stays within 4 MB
-    const int64_t max_sub = std::max<int64_t>(2048, ((int64_t)1 << 20) / std::max(E, 1));
-    int64_t L = 256;
-    while ((N + L - 1) / L > max_sub) L *= 2;
-    pl.L = (int)L;
-    pl.nsub = (int)((N + L - 1) / L);
+    // chunks of C = R * 2^j routes per workgroup, R = one round (16 waves x
+    // RG groups of 64: RG = 4 from 2^20 routes, else 1 so that mid-sized maps
+    // still spread over many workgroups); at most max(2048, 2^20 / E) chunks,
+    // so the per-chunk count matrix stays within 4 MB
+    const int64_t max_chunks = std::max<int64_t>(2048, ((int64_t)1 << 20) / std::max(E, 1));
+    pl.rg = N >= ((int64_t)1 << 20) ? 4 : 1;
+    int64_t C = (int64_t)kBigWaves * 64 * pl.rg;
+    while ((N + C - 1) / C > max_chunks) C *= 2;
+    pl.L = (int)C;
+    pl.nsub = (int)((N + C - 1) / C);
     pl.nbits = 32 - __builtin_clz((unsigned)E);  // bits to hold 0..E (E is the sentinel)
     pl.ws_bytes = (size_t)E * (size_t)pl.nsub * sizeof(int32_t) + (size_t)E * sizeof(int32_t);
     return pl;
@@ -372,16 +443,23 @@ hipError_t launch_sparse_map(const int32_t *ids, int N, int E, int32_t *expert_c
     }
     int32_t *cnt = reinterpret_cast<int32_t *>(workspace);
     int32_t *totals = cnt + (size_t)E * pl.nsub;
-    const int blocks = (pl.nsub + kMapWaves - 1) / kMapWaves;
+    const size_t hist_lds = chunk_hist_lds_bytes(E), assign_lds = chunk_assign_lds_bytes(E, pl.rg);
     prof_begin(stream, kKMapHist);
-    smap_hist_kernel<<<blocks, 256, 0, stream>>>(ids, N, E, pl.nbits, pl.L, pl.nsub, cnt);
+    if (pl.rg == 4)
+        smap_chunk_hist_kernel<4><<<pl.nsub, 1024, hist_lds, stream>>>(ids, N, E, pl.nbits, pl.L, pl.nsub, cnt);
+    else
+        smap_chunk_hist_kernel<1><<<pl.nsub, 1024, hist_lds, stream>>>(ids, N, E, pl.nbits, pl.L, pl.nsub, cnt);
     prof_end(stream, kKMapHist);
     prof_begin(stream, kKMapRowscan);
     smap_rowscan_kernel<<<E, 256, 0, stream>>>(cnt, pl.nsub, totals);
     prof_end(stream, kKMapRowscan);
     prof_begin(stream, kKMapAssign);
-    smap_assign_kernel<<<blocks, 256, 0, stream>>>(ids, N, E, pl.nbits, pl.L, pl.nsub, cnt, totals, expert_counts,
-                                                   expert_offsets, sparse_rows, slot_src);
+    if (pl.rg == 4)
+        smap_chunk_assign_kernel<4><<<pl.nsub, 1024, assign_lds, stream>>>(
+            ids, N, E, pl.nbits, pl.L, pl.nsub, cnt, totals, expert_counts, expert_offsets, sparse_rows, slot_src);
+    else
+        smap_chunk_assign_kernel<1><<<pl.nsub, 1024, assign_lds, stream>>>(
+            ids, N, E, pl.nbits, pl.L, pl.nsub, cnt, totals, expert_counts, expert_offsets, sparse_rows, slot_src);
     prof_end(stream, kKMapAssign);
     return hipGetLastError();
 }

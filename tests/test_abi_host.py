@@ -184,9 +184,25 @@ def test_workspace_has_no_token_replication(lib):
         base = S * k * F * 2 + S * 4096 * 4
         assert base <= d1 <= base + (1 << 20)
     # the router and map workspaces do not scale with D at all
-    assert lib.moe_route_workspace_bytes(4096, 256) == 16 * 4096 * 256 * 4  # 16 K-splits of partial logits
+    assert lib.moe_route_workspace_bytes(4096, 256) == 8 * 4096 * 256 * 4  # 8 K-splits of partial logits
     assert lib.moe_route_workspace_bytes(4096, 8) == 0  # small-E router keeps logits in registers
     assert lib.moe_sparse_map_workspace_bytes(4096, 8, 256) < 1 << 20
+
+
+def test_noalloc_scratch_coverage(lib):
+    """The no-allocation map serves exactly the maps whose workspace fits its 4 MiB + 4 KiB array:
+    every map with E <= 512, every map of fewer than 2^20 routes, and E = 1024 up to 2^22 routes."""
+    limit = (4 << 20) + (4 << 10)
+    ws = lib.moe_sparse_map_workspace_bytes
+    for E in (2, 8, 64, 128, 256, 384, 512):
+        for S, k in ((1 << 21, 4), (1 << 22, 8), (1 << 23, 8), ((1 << 27) - 1, 8), (3000, 7)):
+            assert ws(S, k, E) <= limit, (S, k, E)
+    for E in (513, 600, 777, 1000, 1024):
+        for N in (8193, 100_000, (1 << 20) - 1):
+            assert ws(N, 1, E) <= limit, (N, E)
+    assert ws(1 << 22, 1, 1024) == limit
+    assert ws((1 << 22) + 1, 1, 1024) > limit
+    assert ws(1 << 23, 1, 1024) > limit
 
 
 def test_product_path_does_not_use_oracle():

@@ -60,18 +60,20 @@ def test_noalloc_two_calls_second_smaller(oracle_lib):
     check_against_workspace_call(oracle_lib, ids_for(700, 8, 64, seed=3), 64, "one workgroup (5600 routes)")
 
 
-@pytest.mark.parametrize("S,k,E", [(1 << 21, 4, 128), (1 << 16, 8, 512), (32768, 8, 1024)])
+@pytest.mark.parametrize("S,k,E", [(1 << 21, 4, 128), (1 << 16, 8, 512), (32768, 8, 1024), (1 << 18, 16, 1024)])
 def test_noalloc_largest_covered_maps(oracle_lib, S, k, E):
-    """Maps at the scratch's limits: every map with E <= 512 fits, and E = 1024 up to 2^18 routes."""
+    """Maps at the scratch's limits: every map with E <= 512 fits, and E = 1024 up to 2^22 routes
+    (1024 chunks of 4096 routes: a 4 MiB count matrix, the whole array)."""
     check_against_workspace_call(oracle_lib, ids_for(S, k, E, seed=S + E), E, "at the scratch limit")
 
 
 def test_noalloc_rejects_maps_beyond_the_scratch():
-    """E = 1024 with 2^20 routes needs an 8 MiB count matrix: MOE_ERR_SCRATCH_LIMIT, before anything
+    """E = 1024 with 2^23 routes needs an 8 MiB count matrix: MOE_ERR_SCRATCH_LIMIT, before anything
     is enqueued (the outputs keep their fill)."""
     import sparse_mixture_experts_gemv_amd as smoe
-    S, k, E = 1 << 17, 8, 1024
-    ids = ids_for(S, k, E, seed=4)
+    S, k, E = 1 << 19, 16, 1024
+    g = torch.Generator(device=DEV).manual_seed(4)
+    ids = torch.randint(0, E, (S, k), generator=g, device=DEV, dtype=torch.int32)
     out = outputs(S, k, E, -7)
     st = call_noalloc(ids, E, out)
     torch.cuda.synchronize()
