@@ -15,8 +15,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct SparseMapPlan {
     int L;        // routes per chunk (one workgroup of the multi-pass form)
     int nsub;     // number of chunks
-    int rg;       // groups of 64 routes per wave and round (1 or 4)
-    int nbits;    // id bits examined by match-any (covers the sentinel E)
+    int rg;       // groups of 64 routes per wave and round (1 or 8)
     size_t ws_bytes;
 };
 SparseMapPlan sparse_map_plan(int64_t N, int E);

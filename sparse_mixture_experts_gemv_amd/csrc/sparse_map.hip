@@ -43,9 +43,11 @@ __device__ __forceinline__ unsigned long long match_any(int key, int nbits) {
     return m;
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads); returns the
-// exclusive prefix and writes the block total to *total.
-__device__ int block_exscan_256(int v, int *s_tmp, int *total) {
+// Block-wide exclusive scan of one int per thread (WAVES wavefronts); returns
+// the exclusive prefix and writes the block total to *total. s_tmp holds
+// WAVES ints.
+template <int WAVES>
+__device__ int block_exscan(int v, int *s_tmp, int *total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int x = v;
 #pragma unroll
@@ -57,7 +59,7 @@ __device__ int block_exscan_256(int v, int *s_tmp, int *total) {
     __syncthreads();
     int wave_base = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < WAVES; ++i) {
         if (i < w) wave_base += s_tmp[i];
         tot += s_tmp[i];
     }
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void smap_rowscan_kernel(int32_t *__restrict__
             s += v[i];
         }
         int tot;
-        int pre = block_exscan_256(s, s_tmp, &tot) + running;
+        int pre = block_exscan<4>(s, s_tmp, &tot) + running;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int idx = base + threadIdx.x * 4 + i;
@@ -194,176 +196,213 @@ __global__ __launch_bounds__(1024) void smap_small_kernel(const int32_t *__restr
     }
 }
 
-// ---- large maps: chunks of routes per 1024-thread workgroup ----
+// ---- large maps: chunks of routes per workgroup ----
 //
-// The routes are cut into chunks of C consecutive routes, one per workgroup,
-// walked in rounds of 16 waves x RG groups of 64 routes. The histogram pass
-// counts each chunk's routes per expert (cnt[e][chunk]); after the row scan
-// over chunks, the assignment pass takes each round of its chunk, ranks the
-// round's routes stably by expert in LDS (per-wave counts from match-any,
-// their prefix over the waves, and the prefix over experts), writes
-// sparse_rows in route order and then slot_src from the locally sorted
-// order: the routes of one expert in one round have consecutive slots, so
-// slot_src leaves as runs of consecutive 4-byte words instead of one
-// scattered word per lane. The slots are those of the stable sort, as in
-// every other form of the map.
-constexpr int kBigWaves = 16;
+// The routes are cut into chunks of C consecutive routes, one chunk per
+// workgroup. The histogram pass counts each chunk's routes per expert with
+// LDS atomic adds (cnt[e][chunk]; counts commute, so the order of the adds
+// does not matter). After the row scan over chunks, the assignment pass
+// walks its chunk in rounds of kAssignWaves waves x RG groups of 64 routes
+// (wave w takes the round's w-th run of RG * 64 routes), ranks each round's
+// routes stably by expert (match-any ranks within a group of 64, per-wave
+// counters over the wave's groups, the waves' prefix per expert and the
+// prefix over experts), places them in that order in LDS, writes
+// sparse_rows in route order and then slot_src from the local order: the
+// routes of one expert in one round have consecutive slots, so slot_src
+// leaves as runs of consecutive words instead of one scattered word per
+// lane. The next round's ids are loaded while the current round is ranked.
+constexpr int kHistThreads = 256;
+constexpr int kHistUnroll = 8;  // routes per thread whose ids are in flight together
+constexpr int kAssignWaves = 8;
+constexpr int kAssignThreads = kAssignWaves * 64;
 
-// Exclusive scan of one int per thread over a 1024-thread workgroup; returns
-// the thread's exclusive prefix and the total in *total.
-__device__ int block_exscan_1024(int v, int *s_tmp, int *total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
-    if (lane == 63) s_tmp[w] = x;
+template <int U>
+__global__ __launch_bounds__(kHistThreads) void smap_chunk_hist_kernel(const int32_t *__restrict__ ids, int N, int E,
+                                                                       int C, int nchunks, int32_t *__restrict__ cnt) {
+    extern __shared__ int32_t s_hist[];  // [E]
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kHistThreads) s_hist[e] = 0;
     __syncthreads();
-    int base = 0, tot = 0;
+    // offsets within the chunk, so that no index passes N (N < 2^31)
+    const int *chunk = ids + (size_t)blockIdx.x * C;
+    const int len = min(N - (int)blockIdx.x * C, C);
+    for (int o = 0; o < len; o += kHistThreads * U) {
+        int v[U];
 #pragma unroll
-    for (int i = 0; i < kBigWaves; ++i) {
-        if (i < w) base += s_tmp[i];
-        tot += s_tmp[i];
-    }
-    __syncthreads();
-    *total = tot;
-    return base + x - v;
-}
-
-template <int RG>
-__global__ __launch_bounds__(1024) void smap_chunk_hist_kernel(const int32_t *__restrict__ ids, int N, int E, int nbits,
-                                                               int C, int nchunks, int32_t *__restrict__ cnt) {
-    extern __shared__ int32_t s_cnt[];  // [wave][expert], 16 E ints
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int32_t *my = s_cnt + w * E;
-    for (int e = lane; e < E; e += 64) my[e] = 0;
-    const int base = blockIdx.x * C;
-    const int end = min(N, base + C);
-    constexpr int ROUND = kBigWaves * 64 * RG;
-    for (int r0 = base; r0 < end; r0 += ROUND) {
-        int ev[RG];
-#pragma unroll
-        for (int u = 0; u < RG; ++u) {
-            const int f = r0 + (w * RG + u) * 64 + lane;
-            ev[u] = f < end ? ids[f] : E;
+        for (int u = 0; u < U; ++u) {
+            const int i = o + u * kHistThreads + tid;
+            v[u] = i < len ? chunk[i] : -1;
         }
 #pragma unroll
-        for (int u = 0; u < RG; ++u) {
-            int e = ev[u];
-            if ((unsigned)e >= (unsigned)E) e = E;
-            const unsigned long long m = match_any(e, nbits);
-            if (lane == __ffsll(m) - 1 && e < E) my[e] += __popcll(m);
-        }
+        for (int u = 0; u < U; ++u)
+            if ((unsigned)v[u] < (unsigned)E) atomicAdd(&s_hist[v[u]], 1);  // ids outside [0, E) get no slot
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 1024) {
-        int t = 0;
-        for (int i = 0; i < kBigWaves; ++i) t += s_cnt[i * E + e];
-        cnt[(size_t)e * nchunks + blockIdx.x] = t;
-    }
+    for (int e = tid; e < E; e += kHistThreads) cnt[(size_t)e * nchunks + blockIdx.x] = s_hist[e];
 }
 
-constexpr size_t chunk_hist_lds_bytes(int E) { return (size_t)kBigWaves * E * sizeof(int32_t); }
+constexpr size_t chunk_hist_lds_bytes(int E) { return (size_t)E * sizeof(int32_t); }
 constexpr size_t chunk_assign_lds_bytes(int E, int RG) {
-    return (size_t)(kBigWaves + 2) * E * sizeof(int32_t) + (size_t)kBigWaves * 64 * RG * (sizeof(int32_t) + sizeof(int16_t));
+    return (size_t)kAssignThreads * RG * sizeof(int2) + (size_t)kAssignWaves * E * sizeof(unsigned long long) +
+           (size_t)(kAssignWaves + 2) * E * sizeof(int32_t);
 }
 
 template <int RG>
-__global__ __launch_bounds__(1024) void smap_chunk_assign_kernel(
-    const int32_t *__restrict__ ids, int N, int E, int nbits, int C, int nchunks, const int32_t *__restrict__ cnt,
+__global__ __launch_bounds__(kAssignThreads) void smap_chunk_assign_kernel(
+    const int32_t *__restrict__ ids, int N, int E, int C, int nchunks, const int32_t *__restrict__ cnt,
     const int32_t *__restrict__ totals, int32_t *__restrict__ expert_counts, int32_t *__restrict__ expert_offsets,
     int32_t *__restrict__ sparse_rows, int32_t *__restrict__ slot_src) {
-    constexpr int ROUND = kBigWaves * 64 * RG;
-    // LDS (chunk_assign_lds_bytes): s_wc [16][E] per-wave counts of the round,
-    // then the waves' starts; s_base [E] next slot of expert e in this chunk;
-    // s_lofs [E] start of expert e's run in the round's local order; s_f
-    // [ROUND] the round's routes sorted by expert; s_e [ROUND] their experts
-    extern __shared__ int32_t s_lds[];
-    int32_t *s_wc = s_lds;
-    int32_t *s_base = s_wc + kBigWaves * E;
-    int32_t *s_lofs = s_base + E;
-    int32_t *s_f = s_lofs + E;
-    int16_t *s_e = reinterpret_cast<int16_t *>(s_f + ROUND);
-    __shared__ int s_tmp[kBigWaves];
+    constexpr int T = kAssignThreads, W = kAssignWaves, ROUND = T * RG;
+    constexpr int EPT = (kMaxExperts + T - 1) / T;
+    // LDS (chunk_assign_lds_bytes):
+    //   s_pair [ROUND]  the round's (slot, route) pairs in local order (sorted by expert)
+    //   s_peer [W][E]   per-wave 64-bit lane masks
+    //   s_wc   [W][E]   per-wave counts of the round, then each wave's first
+    //                   local position for expert e
+    //   s_base [E]      next slot of expert e in this chunk
+    //   s_delta[E]      slot - local position, for the round's routes of expert e
+    extern __shared__ int2 s_pair[];
+    unsigned long long *s_peer = reinterpret_cast<unsigned long long *>(s_pair + ROUND);
+    int32_t *s_wc = reinterpret_cast<int32_t *>(s_peer + W * E);
+    int32_t *s_base = s_wc + W * E;
+    int32_t *s_delta = s_base + E;
+    __shared__ int s_tmp[W];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-    // offsets = exclusive scan of the per-expert totals (thread e owns expert e, E <= 1024)
-    {
-        const int e = tid;
-        const int v = e < E ? totals[e] : 0;
-        int tot;
-        const int off = block_exscan_1024(v, s_tmp, &tot);
-        if (e < E) {
-            s_base[e] = off + cnt[(size_t)e * nchunks + blockIdx.x];  // cnt holds the scan over chunks
-            if (blockIdx.x == 0) {
-                expert_counts[e] = v;
-                expert_offsets[e] = off;
-            }
-        }
-        if (blockIdx.x == 0 && e == 0) expert_offsets[E] = tot;
-    }
+    unsigned long long *peer = s_peer + w * E;
     int32_t *my = s_wc + w * E;
+    // route f = base + i of the chunk, 0 <= i < len; indices are formed as
+    // offsets within the chunk, so that none passes N (N < 2^31)
     const int base = blockIdx.x * C;
-    const int end = min(N, base + C);
-    for (int r0 = base; r0 < end; r0 += ROUND) {
-        for (int e = lane; e < E; e += 64) my[e] = 0;
-        // ranks within the wave (groups in order, lanes in order)
-        int ev[RG], rk[RG];
+    const int len = min(N - base, C);
+    const int *chunk = ids + base;
+    int32_t *rows = sparse_rows + base;
+
+    // the first round's ids are in flight while the offsets are formed
+    int ev[RG];
 #pragma unroll
-        for (int u = 0; u < RG; ++u) {
-            const int f = r0 + (w * RG + u) * 64 + lane;
-            ev[u] = f < end ? ids[f] : E;
+    for (int u = 0; u < RG; ++u) {
+        const int i = (w * RG + u) * 64 + lane;
+        ev[u] = i < len ? chunk[i] : -1;
+    }
+    // offsets = exclusive scan of the per-expert totals; thread t owns experts
+    // t * EPT .. t * EPT + EPT - 1 (E <= 1024)
+    {
+        int tv[EPT], cv[EPT], sum = 0;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = tid * EPT + i;
+            tv[i] = e < E ? totals[e] : 0;
+            cv[i] = e < E ? cnt[(size_t)e * nchunks + blockIdx.x] : 0;  // scanned over chunks
+            sum += tv[i];
         }
+        int tot;
+        int off = block_exscan<W>(sum, s_tmp, &tot);
 #pragma unroll
-        for (int u = 0; u < RG; ++u) {
-            int e = ev[u];
-            if ((unsigned)e >= (unsigned)E) e = E;
-            ev[u] = e;
-            const unsigned long long m = match_any(e, nbits);
-            const int leader = __ffsll(m) - 1;
-            int b = (lane == leader && e < E) ? my[e] : 0;
-            b = __shfl(b, leader);
-            rk[u] = b + __popcll(m & lt);
-            if (lane == leader && e < E) my[e] = b + __popcll(m);
-        }
-        __syncthreads();
-        // thread e: the waves' starts within expert e's run, and the run starts (scan over experts)
-        int tot_e = 0;
-        if (tid < E)
-            for (int i = 0; i < kBigWaves; ++i) {
-                const int c = s_wc[i * E + tid];
-                s_wc[i * E + tid] = tot_e;
-                tot_e += c;
-            }
-        int round_total;
-        const int lofs = block_exscan_1024(tid < E ? tot_e : 0, s_tmp, &round_total);
-        if (tid < E) s_lofs[tid] = lofs;
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < RG; ++u) {
-            const int f = r0 + (w * RG + u) * 64 + lane;
-            const int e = ev[u];
+        for (int i = 0; i < EPT; ++i) {
+            const int e = tid * EPT + i;
             if (e < E) {
-                const int lpos = s_lofs[e] + s_wc[w * E + e] + rk[u];
-                s_f[lpos] = f;
-                s_e[lpos] = (int16_t)e;
-                sparse_rows[f] = s_base[e] + (lpos - s_lofs[e]);
-            } else if (f < end) {
-                sparse_rows[f] = -1;  // id outside [0, E): the route gets no slot
+                s_base[e] = off + cv[i];
+                if (blockIdx.x == 0) {
+                    expert_counts[e] = tv[i];
+                    expert_offsets[e] = off;
+                }
+            }
+            off += tv[i];
+        }
+        if (blockIdx.x == 0 && tid == 0) expert_offsets[E] = tot;
+    }
+    for (int o = 0; o < len; o += ROUND) {
+        for (int e = lane; e < E; e += 64) my[e] = 0;
+        // ranks within the wave (groups in order, lanes in order); only lanes
+        // with an id in [0, E) take part. The lanes of one group holding the
+        // same expert find each other through the wave's LDS word peer[e]:
+        // cleared, then each such lane ORs in its own bit, then read back
+        // (a wave's LDS operations complete in issue order, and OR commutes,
+        // so the mask does not depend on the order of the lanes' ORs).
+        int rk[RG];
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            const int e = ev[u];
+            const bool valid = (unsigned)e < (unsigned)E;
+            unsigned long long m = 0;
+            int c = 0;
+            if (valid) peer[e] = 0;
+            __builtin_amdgcn_wave_barrier();
+            if (valid) atomicOr(&peer[e], 1ull << lane);
+            __builtin_amdgcn_wave_barrier();
+            if (valid) {
+                m = peer[e];
+                c = my[e];
+            }
+            __builtin_amdgcn_wave_barrier();
+            rk[u] = c + __popcll(m & lt);
+            if (valid && lane == __ffsll(m) - 1) my[e] = c + __popcll(m);
+            __builtin_amdgcn_wave_barrier();
+        }
+        // the next round's ids
+        int nx[RG];
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            const int i = o + ROUND + (w * RG + u) * 64 + lane;
+            nx[u] = i < len ? chunk[i] : -1;
+        }
+        __syncthreads();
+        // per expert: the run length over the waves, the runs' starts (scan
+        // over experts), then each wave's first position and the slot offset
+        int wc[EPT][W], te[EPT], sum = 0;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = tid * EPT + i;
+            te[i] = 0;
+#pragma unroll
+            for (int v = 0; v < W; ++v) {
+                wc[i][v] = e < E ? s_wc[v * E + e] : 0;
+                te[i] += wc[i][v];
+            }
+            sum += te[i];
+        }
+        int round_total;
+        int lofs = block_exscan<W>(sum, s_tmp, &round_total);
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = tid * EPT + i;
+            if (e < E) {
+                int p = lofs;
+#pragma unroll
+                for (int v = 0; v < W; ++v) {
+                    s_wc[v * E + e] = p;
+                    p += wc[i][v];
+                }
+                const int b = s_base[e];
+                s_delta[e] = b - lofs;
+                s_base[e] = b + te[i];  // read again in the next round's transform
+            }
+            lofs += te[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            const int i = o + (w * RG + u) * 64 + lane;
+            const int e = ev[u];
+            if ((unsigned)e < (unsigned)E) {  // only loaded lanes (i < len) hold ids in [0, E)
+                const int lpos = my[e] + rk[u];
+                const int slot = s_delta[e] + lpos;
+                s_pair[lpos] = make_int2(slot, base + i);
+                rows[i] = slot;
+            } else if (i < len) {
+                rows[i] = -1;  // id outside [0, E): the route gets no slot
             }
         }
         __syncthreads();
         // slot_src from the local order: consecutive positions of one expert are consecutive slots
-        for (int q = tid; q < round_total; q += 1024) {
-            const int e = s_e[q];
-            slot_src[s_base[e] + (q - s_lofs[e])] = s_f[q];
+        for (int q = tid; q < round_total; q += T) {
+            const int2 pr = s_pair[q];
+            slot_src[pr.x] = pr.y;
         }
         __syncthreads();
-        if (tid < E) s_base[tid] += tot_e;
-        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < RG; ++u) ev[u] = nx[u];
     }
 }
 
@@ -376,17 +415,17 @@ __global__ void smap_empty_kernel(int E, int32_t *expert_counts, int32_t *expert
 
 SparseMapPlan sparse_map_plan(int64_t N, int E) {
     SparseMapPlan pl;
-    // chunks of C = R * 2^j routes per workgroup, R = one round (16 waves x
-    // RG groups of 64: RG = 4 from 2^20 routes, else 1 so that mid-sized maps
-    // still spread over many workgroups); at most max(2048, 2^20 / E) chunks,
-    // so the per-chunk count matrix stays within 4 MB
+    // rounds of kAssignThreads * RG routes (RG = 8 from 2^18 routes, else 1
+    // so that mid-sized maps still spread over many workgroups), one round
+    // per chunk, chunks doubled while there would be more than
+    // max(2048, 2^20 / E) of them, so that the per-chunk count matrix stays
+    // within 4 MiB for E <= 512
     const int64_t max_chunks = std::max<int64_t>(2048, ((int64_t)1 << 20) / std::max(E, 1));
-    pl.rg = N >= ((int64_t)1 << 20) ? 4 : 1;
-    int64_t C = (int64_t)kBigWaves * 64 * pl.rg;
+    pl.rg = N >= ((int64_t)1 << 18) ? 8 : 1;
+    int64_t C = (int64_t)kAssignThreads * pl.rg;
     while ((N + C - 1) / C > max_chunks) C *= 2;
     pl.L = (int)C;
     pl.nsub = (int)((N + C - 1) / C);
-    pl.nbits = 32 - __builtin_clz((unsigned)E);  // bits to hold 0..E (E is the sentinel)
     pl.ws_bytes = (size_t)E * (size_t)pl.nsub * sizeof(int32_t) + (size_t)E * sizeof(int32_t);
     return pl;
 }
@@ -430,36 +469,34 @@ hipError_t launch_sparse_map(const int32_t *ids, int N, int E, int32_t *expert_c
         prof_end(stream, kKMapEmpty);
         return hipGetLastError();
     }
-    const SparseMapPlan pl = sparse_map_plan(N, E);
     if (N <= kSmallMapRoutes) {
         // chunks of whole 64 * kMapUnroll groups, one per wave
         constexpr int G = 64 * kMapUnroll;
         const int L = ((N + kSmallMapWaves - 1) / kSmallMapWaves + G - 1) / G * G;
         prof_begin(stream, kKMapSmall);
-        smap_small_kernel<<<1, 1024, 0, stream>>>(ids, N, E, pl.nbits, L, expert_counts, expert_offsets, sparse_rows,
+        const int sbits = 32 - __builtin_clz((unsigned)E);  // bits to hold 0..E (E is the sentinel)
+        smap_small_kernel<<<1, 1024, 0, stream>>>(ids, N, E, sbits, L, expert_counts, expert_offsets, sparse_rows,
                                                   slot_src);
         prof_end(stream, kKMapSmall);
         return hipGetLastError();
     }
+    const SparseMapPlan pl = sparse_map_plan(N, E);
     int32_t *cnt = reinterpret_cast<int32_t *>(workspace);
     int32_t *totals = cnt + (size_t)E * pl.nsub;
     const size_t hist_lds = chunk_hist_lds_bytes(E), assign_lds = chunk_assign_lds_bytes(E, pl.rg);
     prof_begin(stream, kKMapHist);
-    if (pl.rg == 4)
-        smap_chunk_hist_kernel<4><<<pl.nsub, 1024, hist_lds, stream>>>(ids, N, E, pl.nbits, pl.L, pl.nsub, cnt);
-    else
-        smap_chunk_hist_kernel<1><<<pl.nsub, 1024, hist_lds, stream>>>(ids, N, E, pl.nbits, pl.L, pl.nsub, cnt);
+    smap_chunk_hist_kernel<kHistUnroll><<<pl.nsub, kHistThreads, hist_lds, stream>>>(ids, N, E, pl.L, pl.nsub, cnt);
     prof_end(stream, kKMapHist);
     prof_begin(stream, kKMapRowscan);
     smap_rowscan_kernel<<<E, 256, 0, stream>>>(cnt, pl.nsub, totals);
     prof_end(stream, kKMapRowscan);
     prof_begin(stream, kKMapAssign);
-    if (pl.rg == 4)
-        smap_chunk_assign_kernel<4><<<pl.nsub, 1024, assign_lds, stream>>>(
-            ids, N, E, pl.nbits, pl.L, pl.nsub, cnt, totals, expert_counts, expert_offsets, sparse_rows, slot_src);
+    if (pl.rg == 8)
+        smap_chunk_assign_kernel<8><<<pl.nsub, kAssignThreads, assign_lds, stream>>>(
+            ids, N, E, pl.L, pl.nsub, cnt, totals, expert_counts, expert_offsets, sparse_rows, slot_src);
     else
-        smap_chunk_assign_kernel<1><<<pl.nsub, 1024, assign_lds, stream>>>(
-            ids, N, E, pl.nbits, pl.L, pl.nsub, cnt, totals, expert_counts, expert_offsets, sparse_rows, slot_src);
+        smap_chunk_assign_kernel<1><<<pl.nsub, kAssignThreads, assign_lds, stream>>>(
+            ids, N, E, pl.L, pl.nsub, cnt, totals, expert_counts, expert_offsets, sparse_rows, slot_src);
     prof_end(stream, kKMapAssign);
     return hipGetLastError();
 }
