@@ -60,6 +60,8 @@ struct GemmParams {
     const int4 *tiles;        // [n_mtiles] (expert, row_begin, row_end, -) ; expert < 0 = empty
     const uint32_t *order;    // [n_mtiles * n_ntiles] block order: mt | nt << kOrderMtBits, valid blocks first
     const int *valid_mtiles;  // device count of non-empty M tiles
+    int *queue;               // per-XCD tile claim counters, kQueueStride ints apart (zeroed by the
+                              // tile table), for the persistent kernel's dynamic form
     void *C;                  // h bf16 [S*k, N] / acc fp32 [S, N] / y fp32 [S*k, N] / logits fp32 [S, N]
                               // / a|b bf16 [S*k, 2N] (kGateUpSave, kSwigluBwd)
     void *C2;                 // h bf16 [S*k, N] (kGateUpSave)

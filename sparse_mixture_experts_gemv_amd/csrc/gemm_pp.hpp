@@ -634,10 +634,68 @@ __device__ __forceinline__ bool pp_full_tile(const GemmParams &p, int mt) {
     return t.z - t.y == BM;
 }
 
+// Logical block L of the order: its tile, in the short-tile form where that
+// is enabled and the tile holds fewer than BM rows.
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A, bool SKIP_ROWS, int FLAGS>
+__device__ __forceinline__ void pp_block(const GemmParams &p, char *smem, int L) {
+    const uint32_t v = p.order[L];
+    const int mt = (int)(v & kOrderMtMask), nt = (int)(v >> kOrderMtBits);
+    if (mt >= p.n_mtiles) return;
+    if (!SKIP_ROWS || pp_full_tile<BM, MODE>(p, mt))
+        pp_tile<BM, BN, MODE, BK, STAGES, STAGES_A, false, FLAGS>(p, smem, mt, nt, 0, p.K / BK);
+    else
+        pp_tile<BM, BN, MODE, BK, STAGES, STAGES_A, true, FLAGS>(p, smem, mt, nt, 0, p.K / BK);
+}
+
+// Dynamic tile scheduling. The logical blocks 0 .. total-1 of the order are
+// cut into kNumXcd contiguous queues, queue x holding [x total / 8,
+// (x + 1) total / 8); the workgroups of XCD x (workgroups are dispatched to
+// the XCDs round-robin by block index) claim the blocks of queue x in order,
+// so the blocks that share a weight panel run together on one XCD's L2. A
+// workgroup whose queue is exhausted looks at every queue's counter and
+// steals from the nearest one with blocks left. Claims are agent-scope
+// atomic adds on counters the tile table zeroed; every block is handed out
+// exactly once, whichever workgroup or XCD takes it.
+__device__ __forceinline__ int queue_begin(int q, int total) {
+    return (int)(((long long)total * q) / kNumXcd);
+}
+
+// Called by all 64 lanes of one wave; returns a wave-uniform logical block,
+// or total when every queue is exhausted. Each failed claim finds its queue
+// exhausted (counters only grow), and the wave's own later loads of that
+// counter see at least its own add, so it fails on each queue at most once:
+// the loop ends after at most kNumXcd + 1 claims.
+__device__ __forceinline__ int queue_claim(int *ctr, int home, int total) {
+    const int lane = threadIdx.x & 63;
+    int q = home;
+    for (int tries = 0; tries < 4 * kNumXcd; ++tries) {
+        int c = 0;
+        if (lane == 0) c = atomicAdd(ctr + q * kQueueStride, 1);
+        c = __builtin_amdgcn_readfirstlane(c);
+        const int b = queue_begin(q, total);
+        if (c < queue_begin(q + 1, total) - b) return b + c;
+        int left = 0;
+        if (lane < kNumXcd) {
+            const int cq = __hip_atomic_load(ctr + lane * kQueueStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            left = cq < queue_begin(lane + 1, total) - queue_begin(lane, total);
+        }
+        const unsigned m = (unsigned)__ballot(left) & ((1u << kNumXcd) - 1u);
+        if (m == 0) return total;
+        const unsigned rot = ((m >> home) | (m << (kNumXcd - home))) & ((1u << kNumXcd) - 1u);
+        q = (home + __builtin_ctz(rot)) % kNumXcd;
+    }
+    return total;
+}
+
 // Persistent tile-granular form: one workgroup per CU walks the valid
-// blocks of the order table with stride gridDim.x (each XCD takes one
-// contiguous run of the order per round), so a tile's epilogue stores drain
-// while the same workgroup already streams its next tile.
+// blocks of the order, so a tile's epilogue stores drain while the same
+// workgroup already streams its next tile. Without a queue it takes them
+// with stride gridDim.x (each XCD takes one contiguous run of the order per
+// round); with QUEUE (p.queue then holds the counters) it claims them
+// dynamically as above: wave 4 (which issues
+// no LDS DMA) claims the next block before each tile, while the other group
+// waits for the tile's first k-step to land, and hands it over through LDS
+// once the tile has finished with the ring.
 //
 // With SKIP_ROWS, tiles holding fewer than BM rows run pp_tile's PARTIAL form
 // (a second copy of the main loop). Measured, that pays where many tiles are
@@ -645,19 +703,32 @@ __device__ __forceinline__ bool pp_full_tile(const GemmParams &p, int mt) {
 // tiles over experts of ~210-300 rows: -4 %) and is neutral on the 256-row
 // gate+up tile where nearly all tiles are full; other launches over mostly
 // full tiles leave it off (the second loop copy has cost up to ~3 % there).
-template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool SKIP_ROWS = false, int FLAGS = 0>
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool SKIP_ROWS = false, int FLAGS = 0,
+          bool QUEUE = false>
 __global__ __launch_bounds__(512) void grouped_gemm_pp_persistent_kernel(const GemmParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[PPGeom<BM, BN, MODE, BK, STAGES, STAGES_A>::SMEM];
     const int total = (*p.valid_mtiles) * p.n_ntiles;
-    const int G = gridDim.x;
-    for (int L = xcd_remap(blockIdx.x, G); L < total; L += G) {
-        const uint32_t v = p.order[L];
-        const int mt = (int)(v & kOrderMtMask), nt = (int)(v >> kOrderMtBits);
-        if (mt >= p.n_mtiles) continue;
-        if (!SKIP_ROWS || pp_full_tile<BM, MODE>(p, mt))
-            pp_tile<BM, BN, MODE, BK, STAGES, STAGES_A, false, FLAGS>(p, smem, mt, nt, 0, p.K / BK);
-        else
-            pp_tile<BM, BN, MODE, BK, STAGES, STAGES_A, true, FLAGS>(p, smem, mt, nt, 0, p.K / BK);
+    if constexpr (!QUEUE) {
+        const int G = gridDim.x;
+        for (int L = xcd_remap(blockIdx.x, G); L < total; L += G)
+            pp_block<BM, BN, MODE, BK, STAGES, STAGES_A, SKIP_ROWS, FLAGS>(p, smem, L);
+        return;
+    }
+    const int home = blockIdx.x % kNumXcd;
+    const bool claimer = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 4;  // wave-uniform branch
+    int *handoff = reinterpret_cast<int *>(smem);
+    int next = 0;
+    if (claimer) next = queue_claim(p.queue, home, total);
+    // every round but the last runs a block no other round runs
+    for (;;) {
+        if (claimer && (threadIdx.x & 63) == 0) *handoff = next;
+        __syncthreads();
+        const int L = __builtin_amdgcn_readfirstlane(*handoff);  // uniform: tile fields stay scalar
+        __syncthreads();  // the hand-off slot is part of the ring the tile's DMA fills
+        if (L >= total) break;
+        if (claimer) next = queue_claim(p.queue, home, total);
+        pp_block<BM, BN, MODE, BK, STAGES, STAGES_A, SKIP_ROWS, FLAGS>(p, smem, L);
+        __syncthreads();  // every wave is done with the ring before the slot is written
     }
 }
 

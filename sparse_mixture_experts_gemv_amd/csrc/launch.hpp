@@ -42,7 +42,8 @@ struct FfnPlan {
     int n_mtiles_up, n_mtiles_down;  // upper bounds on M tiles over all experts
     int n_ntiles_up, n_ntiles_down;
     // acc_off: fp32 [S, D] token accumulator (atomic) or fp32 [S*k, D] per-route rows
-    size_t tiles_up_off, tiles_down_off, order_up_off, order_down_off, counts_off, h_off, acc_off, ws_bytes;
+    size_t tiles_up_off, tiles_down_off, order_up_off, order_down_off, counts_off, queue_off, h_off, acc_off,
+        ws_bytes;
 };
 FfnPlan ffn_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k, bool atomic);
 // Whether the plan's tile counts fit the block-order entries.
@@ -59,7 +60,12 @@ struct TileTableArgs {
     int4 *tiles[2];
     uint32_t *order[2];
     int *valid[2];  // number of non-empty M tiles
+    int *queue[2];  // tile claim counters of the GEMM (kQueueInts ints) to zero, or NULL
 };
+// Tile claim counters of one dynamically scheduled GEMM: one per XCD, each on
+// its own 64-byte line.
+constexpr int kQueueStride = 16;
+constexpr int kQueueInts = 8 * kQueueStride;
 void launch_tile_table(const int32_t *offsets, int E, int N, const TileTableArgs &a, hipStream_t stream);
 // out[t] = bf16(sum_j y[t k + j]) (fp32 rows [S*k, D] -> bf16 [S, D]), j in order
 void launch_combine_rows(const float *y, uint16_t *out, int S, int D, int k, hipStream_t stream);
