@@ -25,9 +25,10 @@
 namespace smoe {
 
 // One thread per expert computes ceil(rows / bm) tiles, an exclusive scan
-// gives each expert its first tile T_e, and the expert writes its
-// (expert, row_begin, row_end) entries. The block order is then filled by all
-// threads: blocks [T_e * nn, (T_e + c_e) * nn) belong to expert e (c_e its
+// gives each expert its first tile T_e, and (in workgroup 0) the expert
+// writes its (expert, row_begin, row_end) entries. The block order is then
+// filled by the threads of every workgroup, each workgroup having formed the
+// same T_e: blocks [T_e * nn, (T_e + c_e) * nn) belong to expert e (c_e its
 // tile count, nn the N tiles), N tile major, the expert's M tiles minor; a
 // thread finds the expert of a block by binary search over T_e. Two GEMMs
 // (tile heights) are handled in one launch. Entries past the real tile count
@@ -69,13 +70,15 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restr
         if (e < E) s_first[q][e] = min(base, valid);
         if (e == 0) {
             s_first[q][E] = valid;
-            *a.valid[q] = valid;
+            if (blockIdx.x == 0) *a.valid[q] = valid;
         }
-        const int cnt = min(t[q], max(nm - base, 0));
-        for (int i = 0; i < cnt; ++i)
-            a.tiles[q][base + i] = make_int4(e, off + i * a.bm[q], min(off + (i + 1) * a.bm[q], end), 0);
-        for (int j = valid + threadIdx.x; j < nm; j += 1024) a.tiles[q][j] = make_int4(-1, 0, 0, 0);
-        if (a.queue[q] && threadIdx.x < kQueueInts) a.queue[q][threadIdx.x] = 0;
+        if (blockIdx.x == 0) {
+            const int cnt = min(t[q], max(nm - base, 0));
+            for (int i = 0; i < cnt; ++i)
+                a.tiles[q][base + i] = make_int4(e, off + i * a.bm[q], min(off + (i + 1) * a.bm[q], end), 0);
+            for (int j = valid + threadIdx.x; j < nm; j += 1024) a.tiles[q][j] = make_int4(-1, 0, 0, 0);
+            if (a.queue[q] && threadIdx.x < kQueueInts) a.queue[q][threadIdx.x] = 0;
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restr
         const int nm = a.n_mtiles[q], nn = a.n_ntiles[q];
         const int valid = s_first[q][E];
         const size_t vblocks = (size_t)valid * nn;
-        for (size_t L = threadIdx.x; L < (size_t)nm * nn; L += 1024) {
+        for (size_t L = (size_t)blockIdx.x * 1024 + threadIdx.x; L < (size_t)nm * nn; L += (size_t)gridDim.x * 1024) {
             uint32_t v = kOrderMtMask;
             if (L < vblocks) {
                 // expert: the last e with T_e * nn <= L (experts with no tiles share T_e)
@@ -146,7 +149,10 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float4 *__restr
 
 void launch_tile_table(const int32_t *offsets, int E, int N, const TileTableArgs &a, hipStream_t stream) {
     prof_begin(stream, kKTileTable);
-    tile_table_kernel<<<1, 1024, 0, stream>>>(offsets, E, N, a);
+    // one workgroup per 4096 order entries of the larger table (at most 64)
+    const size_t entries = std::max((size_t)a.n_mtiles[0] * a.n_ntiles[0], (size_t)a.n_mtiles[1] * a.n_ntiles[1]);
+    const int grid = (int)std::min<size_t>(64, std::max<size_t>(1, (entries + 4095) / 4096));
+    tile_table_kernel<<<grid, 1024, 0, stream>>>(offsets, E, N, a);
     prof_end(stream, kKTileTable);
 }
 

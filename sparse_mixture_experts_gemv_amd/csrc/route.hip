@@ -16,7 +16,7 @@
 //    (plain-rows mode), split over K so that a few thousand tokens still
 //    fill the GPU; every split writes its partial logits to the workspace and
 //    topk_softmax_kernel adds the splits in a fixed order (deterministic),
-//    one wavefront per token.
+//    16 lanes per token.
 #include <math.h>
 
 #include "gemm.hpp"
@@ -134,58 +134,59 @@ __global__ __launch_bounds__(256) void route_small_kernel(const uint16_t *__rest
     }
 }
 
-// logits = sum over `nsplit` partial sums [nsplit][S][E] (fixed order).
+// logits = sum over `nsplit` partial sums [nsplit][S][E] (fixed order), then
+// top-k (descending, ties to the lower expert id) and the softmax over the k
+// selected logits. A group of 16 lanes serves one token (4 tokens per wave):
+// lane l holds experts l, l + 16, ..., so each round of the selection is a
+// scan of 16 register values and a 4-step reduction within the group.
+constexpr int kTopkLanes = 16;
+
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restrict__ partial, int nsplit, int S, int E,
                                                            int k, int32_t *__restrict__ ids,
                                                            float *__restrict__ weights) {
-    const int lane = threadIdx.x & 63;
-    const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (s >= S) return;
-    constexpr int NV = kRouteMaxE / 64;
+    constexpr int G = kTopkLanes, NV = kRouteMaxE / G;
+    const int l = threadIdx.x & (G - 1);
+    const int s = blockIdx.x * (256 / G) + (threadIdx.x / G);
+    const int sr = min(s, S - 1);  // groups past S read a valid row and write nothing
     float v[NV];
-    unsigned taken = 0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        v[i] = 0.f;
-        if (lane + 64 * i >= E) taken |= 1u << i;
-    }
+    for (int j = 0; j < NV; ++j) v[j] = 0.f;
     // splits are added in order; four splits of loads are in flight at a time
     for (int q0 = 0; q0 < nsplit; q0 += 4) {
         float t[4][NV];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int e = lane + 64 * i;
-                t[u][i] = (q0 + u < nsplit && e < E) ? partial[((size_t)(q0 + u) * S + s) * E + e] : 0.f;
+            for (int j = 0; j < NV; ++j) {
+                const int e = l + G * j;
+                t[u][j] = (q0 + u < nsplit && e < E) ? partial[((size_t)(q0 + u) * S + sr) * E + e] : 0.f;
             }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int i = 0; i < NV; ++i) v[i] += t[u][i];
+            for (int j = 0; j < NV; ++j) v[j] += t[u][j];
     }
+    unsigned taken = 0;  // bit j: slot j already selected, or past E
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-        if ((taken >> i) & 1u) v[i] = -INFINITY;
+    for (int j = 0; j < NV; ++j)
+        if (l + G * j >= E) taken |= 1u << j;
     float top[kRouteMaxK];
     int topi[kRouteMaxK];
 #pragma unroll
-    for (int j = 0; j < kRouteMaxK; ++j) {
-        top[j] = -INFINITY;
-        topi[j] = 0;
-        if (j < k) {
+    for (int r = 0; r < kRouteMaxK; ++r) {
+        top[r] = -INFINITY;
+        topi[r] = 0;
+        if (r < k) {
             float bv = -INFINITY;
             int bi = 0x7fffffff;
 #pragma unroll
-            for (int i = 0; i < kRouteMaxE / 64; ++i) {
-                const int e = lane + 64 * i;
-                if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-                    bv = v[i];
-                    bi = e;
+            for (int j = 0; j < NV; ++j)  // experts ascend with j: an equal later value never wins
+                if (!((taken >> j) & 1u) && v[j] > bv) {
+                    bv = v[j];
+                    bi = l + G * j;
                 }
-            }
 #pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) {
+            for (int d = G / 2; d >= 1; d >>= 1) {
                 const float ov = __shfl_xor(bv, d);
                 const int oi = __shfl_xor(bi, d);
                 if (ov > bv || (ov == bv && oi < bi)) {
@@ -193,21 +194,21 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
                     bi = oi;
                 }
             }
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-            top[j] = bv;
-            topi[j] = bi;
+            if (bi < E && (bi & (G - 1)) == l) taken |= 1u << (bi / G);
+            top[r] = bv;
+            topi[r] = bi;
         }
     }
     const float m = top[0];
     float z = 0.f;
 #pragma unroll
-    for (int j = 0; j < kRouteMaxK; ++j)
-        if (j < k) z += expf(top[j] - m);
+    for (int r = 0; r < kRouteMaxK; ++r)
+        if (r < k) z += expf(top[r] - m);
 #pragma unroll
-    for (int j = 0; j < kRouteMaxK; ++j) {
-        if (j < k && lane == j) {
-            ids[(size_t)s * k + j] = topi[j];
-            weights[(size_t)s * k + j] = expf(top[j] - m) / z;
+    for (int r = 0; r < kRouteMaxK; ++r) {
+        if (r < k && l == r && s < S) {
+            ids[(size_t)s * k + r] = topi[r];
+            weights[(size_t)s * k + r] = expf(top[r] - m) / z;
         }
     }
 }
@@ -285,7 +286,8 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *w_gate, int S, int D,
     else route_logits_kernel<256><<<blocks, 512, 0, stream>>>(p, pl.nsplit, partial);
     prof_end(stream, kKRouteLogits);
     prof_begin(stream, kKRouteTopk);
-    topk_softmax_kernel<<<(S + 3) / 4, 256, 0, stream>>>(partial, pl.nsplit, S, E, k, topk_ids, topk_weights);
+    topk_softmax_kernel<<<(S + 256 / kTopkLanes - 1) / (256 / kTopkLanes), 256, 0, stream>>>(
+        partial, pl.nsplit, S, E, k, topk_ids, topk_weights);
     prof_end(stream, kKRouteTopk);
     return hipGetLastError();
 }
