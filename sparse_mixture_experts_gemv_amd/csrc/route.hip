@@ -137,39 +137,50 @@ __global__ __launch_bounds__(256) void route_small_kernel(const uint16_t *__rest
 // logits = sum over `nsplit` partial sums [nsplit][S][E] (fixed order), then
 // top-k (descending, ties to the lower expert id) and the softmax over the k
 // selected logits. A group of 16 lanes serves one token (4 tokens per wave):
-// lane l holds experts l, l + 16, ..., so each round of the selection is a
-// scan of 16 register values and a 4-step reduction within the group.
+// lane l holds experts 4 l + c + 64 j (c < 4, j < 4), loaded as 16-byte
+// pieces (E is a multiple of 8, so a piece lies wholly below E or wholly past
+// it), so each round of the selection is a scan of 16 register values in
+// ascending expert order and a 4-step reduction within the group.
 constexpr int kTopkLanes = 16;
 
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restrict__ partial, int nsplit, int S, int E,
                                                            int k, int32_t *__restrict__ ids,
                                                            float *__restrict__ weights) {
-    constexpr int G = kTopkLanes, NV = kRouteMaxE / G;
+    constexpr int G = kTopkLanes, NJ = kRouteMaxE / (4 * G);  // 4 pieces of 4 experts per lane
     const int l = threadIdx.x & (G - 1);
     const int s = blockIdx.x * (256 / G) + (threadIdx.x / G);
     const int sr = min(s, S - 1);  // groups past S read a valid row and write nothing
-    float v[NV];
+    float v[NJ][4];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = 0.f;
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[j][c] = 0.f;
     // splits are added in order; four splits of loads are in flight at a time
     for (int q0 = 0; q0 < nsplit; q0 += 4) {
-        float t[4][NV];
+        float4 t[4][NJ];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                const int e = l + G * j;
-                t[u][j] = (q0 + u < nsplit && e < E) ? partial[((size_t)(q0 + u) * S + sr) * E + e] : 0.f;
+            for (int j = 0; j < NJ; ++j) {
+                const int e = 4 * l + 64 * j;
+                t[u][j] = (q0 + u < nsplit && e < E)
+                              ? *reinterpret_cast<const float4 *>(partial + ((size_t)(q0 + u) * S + sr) * E + e)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int j = 0; j < NV; ++j) v[j] += t[u][j];
+            for (int j = 0; j < NJ; ++j) {
+                v[j][0] += t[u][j].x;
+                v[j][1] += t[u][j].y;
+                v[j][2] += t[u][j].z;
+                v[j][3] += t[u][j].w;
+            }
     }
-    unsigned taken = 0;  // bit j: slot j already selected, or past E
+    unsigned taken = 0;  // bit 4 j + c: expert 4 l + c + 64 j already selected, or past E
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-        if (l + G * j >= E) taken |= 1u << j;
+    for (int j = 0; j < NJ; ++j)
+        if (4 * l + 64 * j >= E) taken |= 15u << (4 * j);
     float top[kRouteMaxK];
     int topi[kRouteMaxK];
 #pragma unroll
@@ -180,11 +191,13 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
             float bv = -INFINITY;
             int bi = 0x7fffffff;
 #pragma unroll
-            for (int j = 0; j < NV; ++j)  // experts ascend with j: an equal later value never wins
-                if (!((taken >> j) & 1u) && v[j] > bv) {
-                    bv = v[j];
-                    bi = l + G * j;
-                }
+            for (int j = 0; j < NJ; ++j)  // experts ascend with (j, c): an equal later value never wins
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (!((taken >> (4 * j + c)) & 1u) && v[j][c] > bv) {
+                        bv = v[j][c];
+                        bi = 4 * l + c + 64 * j;
+                    }
 #pragma unroll
             for (int d = G / 2; d >= 1; d >>= 1) {
                 const float ov = __shfl_xor(bv, d);
@@ -194,7 +207,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
                     bi = oi;
                 }
             }
-            if (bi < E && (bi & (G - 1)) == l) taken |= 1u << (bi / G);
+            if (bi < E && ((bi >> 2) & (G - 1)) == l) taken |= 1u << (4 * (bi >> 6) + (bi & 3));
             top[r] = bv;
             topi[r] = bi;
         }

@@ -52,7 +52,8 @@ def test_route_configs(oracle_lib, name):
 
 @pytest.mark.parametrize("S,D,E,k", [(1, 64, 8, 1), (37, 128, 16, 3), (300, 192, 64, 8), (129, 256, 256, 16),
                                      (1000, 512, 96, 6), (65, 64, 8, 8),
-                                     (50, 640, 16, 4), (19, 4096, 8, 2), (2053, 1152, 128, 4)])
+                                     (50, 640, 16, 4), (19, 4096, 8, 2), (2053, 1152, 128, 4),
+                                     (333, 192, 24, 5), (77, 256, 200, 16), (40, 128, 248, 11)])
 def test_route_shapes(oracle_lib, S, D, E, k):
     cfg = wl.MoEConfig("route", 90 + E, S, D, 64, E, k, None)
     check_route(oracle_lib, wl.gen_x(cfg).to(DEV), wl.gen_w_gate(cfg).to(DEV), k, f"shape {S}x{D}x{E}")
