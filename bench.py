@@ -490,7 +490,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the dropless MoE forward here runs on a single MI355X "
-              "(expert- or token-parallel sharding is described in DESIGN.md, not built). Use --gpus 1.",
+              "(expert- or token-parallel sharding is not built). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
