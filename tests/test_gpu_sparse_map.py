@@ -47,6 +47,30 @@ def test_small_and_general_paths(oracle_lib, E):
         check_exact(oracle_lib, ids, E, "path edge")
 
 
+@pytest.mark.parametrize("E", [8, 1024])
+def test_round_size_edge(oracle_lib, E):
+    """From 2^18 routes the three-pass map switches from rounds of 512 routes
+    (one per chunk) to rounds of 4096: both sides of that edge, ragged."""
+    for S, k in [((1 << 18) - 1, 1), (1 << 18, 1), ((1 << 17) + 1, 2), ((1 << 16) + 3, 4)]:
+        ids = np.random.default_rng(S + E).integers(0, E, size=(S, k), dtype=np.int32)
+        check_exact(oracle_lib, ids, E, "round-size edge")
+
+
+@pytest.mark.parametrize("E,skewed", [(1024, False), (600, True)])
+def test_chunks_of_several_rounds(oracle_lib, E, skewed):
+    """Past 2^23 routes with E >= 512 the count matrix would need more than
+    2048 chunks, so each chunk holds two rounds of 4096 routes (the second
+    round's ids load while the first is ranked) and the last chunk is
+    ragged: 2^20 + 777 tokens x 9 routes."""
+    S, k = (1 << 20) + 777, 9
+    rng = np.random.default_rng(E)
+    if skewed:  # a few hot experts
+        ids = np.minimum((E * rng.power(4.0, size=(S, k))).astype(np.int32), E - 1)
+    else:
+        ids = rng.integers(0, E, size=(S, k), dtype=np.int32)
+    check_exact(oracle_lib, ids, E, "two rounds per chunk")
+
+
 @pytest.mark.parametrize("name", ["tiny", "mixtral", "gptoss", "dsv3", "qwen2"])
 def test_config_shapes(oracle_lib, name):
     cfg = wl.CONFIGS[name]
