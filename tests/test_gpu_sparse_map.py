@@ -111,17 +111,27 @@ def test_degenerate(oracle_lib):
     assert not counts.any() and not offsets.any()
 
 
-def test_invalid_ids_get_no_slot(oracle_lib):
-    ids = wl.gen_random_ids(300, 2, 8, seed=3)
-    bad = ids.copy()
-    bad[10, 1] = 8
-    bad[20, 0] = -1
-    counts, offsets, rows, src = run_map(bad, 8)
-    assert rows[21] == -1 and rows[40] == -1
-    keep = np.ones(600, bool)
-    keep[[21, 40]] = False
-    ref_src = np.nonzero(keep)[0][np.argsort(bad.ravel()[keep], kind="stable")]
-    assert offsets[-1] == 598 and np.array_equal(src[:598], ref_src)
+@pytest.mark.parametrize("S,E", [(300, 8), (20000, 64), (300000, 128)])
+def test_invalid_ids_get_no_slot(oracle_lib, S, E):
+    """Ids outside [0, E) (a precondition violation) get sparse_rows = -1 and
+    no slot; the other routes keep the stable order (one-workgroup map, and
+    both round sizes of the three-pass map)."""
+    bad = wl.gen_random_ids(S, 2, E, seed=3).ravel()
+    rng = np.random.default_rng(S)
+    pos = rng.choice(bad.size, size=max(2, bad.size // 97), replace=False)
+    bad[pos[::2]] = E + rng.integers(0, 5, size=pos[::2].size)
+    bad[pos[1::2]] = -1 - rng.integers(0, 5, size=pos[1::2].size)
+    counts, offsets, rows, src = run_map(bad.reshape(S, 2), E)
+    keep = np.ones(bad.size, bool)
+    keep[pos] = False
+    assert np.all(rows[pos] == -1)
+    ref_src = np.nonzero(keep)[0][np.argsort(bad[keep], kind="stable")]
+    n = int(keep.sum())
+    assert offsets[-1] == n and np.array_equal(src[:n], ref_src)
+    ref_rows = np.full(bad.size, -1, np.int64)
+    ref_rows[ref_src] = np.arange(n)
+    assert np.array_equal(rows, ref_rows)
+    assert np.array_equal(counts, np.bincount(bad[keep], minlength=E))
 
 
 def test_deterministic():
