@@ -689,12 +689,13 @@ __device__ __forceinline__ int queue_claim(int *ctr, int home, int total) {
 
 // Persistent tile-granular form: one workgroup per CU walks the valid
 // blocks of the order, so a tile's epilogue stores drain while the same
-// workgroup already streams its next tile. Without a queue it takes them
-// with stride gridDim.x (each XCD takes one contiguous run of the order per
-// round); with QUEUE (p.queue then holds the counters) it claims them
-// dynamically as above: wave 4 (which issues
-// no LDS DMA) claims the next block before each tile, while the other group
-// waits for the tile's first k-step to land, and hands it over through LDS
+// workgroup already streams its next tile. Without QUEUE it takes them with
+// stride gridDim.x (each XCD takes one contiguous run of the order per
+// round). With QUEUE (p.queue then holds the counters) it claims them
+// dynamically as above: wave 4, which issues no LDS DMA (so its wait for
+// the claim does not touch the DMA waves' vmcnt bookkeeping), claims the
+// next block before each tile while the DMA group waits for the tile's
+// first k-step to land, and hands it over through the first word of LDS
 // once the tile has finished with the ring.
 //
 // With SKIP_ROWS, tiles holding fewer than BM rows run pp_tile's PARTIAL form
