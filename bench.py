@@ -51,10 +51,17 @@ KERNEL_SOURCES = ["sparse_mixture_experts_gemv_amd/csrc/gemm.hpp", "sparse_mixtu
 
 
 def kernel_source_hash() -> str:
+    """Hash of the gate+up kernel's sources with comments and blank lines removed (a comment
+    edit does not invalidate counters taken on the same code)."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            code = re.sub(r"//.*", "", line).strip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
