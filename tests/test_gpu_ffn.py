@@ -81,6 +81,21 @@ def test_ffn_decode_sizes_all_tokens(oracle_lib, S, D, F, E, k, skew, atomic):
     assert_close(got, ref, f"decode ffn {S}x{D}x{F} E={E} k={k} {'atomic' if atomic else 'rows'}", configured=False)
 
 
+@pytest.mark.parametrize("S,E,skew", [(3000, 32, 1.5), (6000, 64, 2.0), (700, 8, 3.0)])
+def test_ffn_uneven_tiles_all_tokens(oracle_lib, S, E, skew):
+    """Zipf-skewed routing: hot experts span many full tiles, cold ones a
+    single short tile, so the gate+up GEMM's per-XCD tile queues empty at
+    very different times and workgroups steal from other XCDs' queues;
+    every token is compared (the ordered combine, as the benchmark runs)."""
+    cfg = wl.MoEConfig("uneven", 80 + E, S, 256, 1024, E, 2, None)
+    p = make_problem(cfg)
+    ids = wl.gen_random_ids(S, 2, E, seed=S + E, skew=skew)
+    w = np.random.default_rng(S).dirichlet(np.ones(2), size=S).astype(np.float32)
+    got = gpu_ffn(p, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+    ref = oracle_ffn_rows(oracle_lib, p, ids, w, np.arange(S))
+    assert_close(got, ref, f"uneven tiles S={S} E={E} skew={skew}", configured=False)
+
+
 @pytest.mark.parametrize("atomic", [False, True], ids=["rows", "atomic"])
 def test_ffn_skewed_single_expert(oracle_lib, atomic):
     """All routes on two experts: one expert spans many M tiles, the rest are empty."""
