@@ -156,7 +156,8 @@ int moe_sparse_map_noalloc(const int32_t *topk_ids, int32_t S, int32_t k, int32_
 /*
  * Workspace bytes for the default combine of moe_scatter_ffn_fwd: the
  * intermediate h [S*k, F] bf16 in slot order, the router-weighted down
- * projection of every route y [S*k, D] fp32 and a tile table. The input
+ * projection of every route y [S*k, D] fp32, a tile table and the gate+up
+ * GEMM's tile-claim counters (rewritten by every call). The input
  * token rows are never replicated (x is read in place by index). Pure host
  * function.
  */
@@ -193,6 +194,9 @@ size_t moe_scatter_ffn_workspace_bytes_atomic(int32_t S, int32_t D, int32_t F, i
  * matrix is [D_in, D_out] with D_out contiguous); topk_weights [S, k] fp32;
  * expert_offsets [E+1] and slot_src [S*k] from moe_sparse_map on the same
  * ids; out [S, D] bf16 (fully written).
+ * The gate+up tiles are handed out at run time from per-XCD queues whose
+ * counters live in the workspace, so two calls in flight at once (on
+ * different streams) need different workspaces, as for h and y.
  * Limits: D % 64 == 0, F % 64 == 0, E <= 1024, S*D < 2^30, D*F < 2^30
  * (32-bit buffer offsets), D <= 2^19, F <= 2^19 and fewer than 2^20 - 1 row
  * tiles (always true for S*k < 2^26): else UNSUPPORTED.
