@@ -26,7 +26,10 @@ namespace smoe {
 
 // One thread per expert computes ceil(rows / bm) tiles, an exclusive scan
 // gives each expert its first tile T_e, and (in workgroup 0) the expert
-// writes its (expert, row_begin, row_end) entries. The block order is then
+// writes its (expert, row_begin, row_end) entries: bm rows per tile and the
+// rest in the last, or (split) the rows shared evenly over the same number
+// of tiles, so that no tile of the expert is much shorter than the others.
+// The block order is then
 // filled by the threads of every workgroup, each workgroup having formed the
 // same T_e: blocks [T_e * nn, (T_e + c_e) * nn) belong to expert e (c_e its
 // tile count, nn the N tiles), N tile major, the expert's M tiles minor; a
@@ -74,8 +77,12 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restr
         }
         if (blockIdx.x == 0) {
             const int cnt = min(t[q], max(nm - base, 0));
-            for (int i = 0; i < cnt; ++i)
-                a.tiles[q][base + i] = make_int4(e, off + i * a.bm[q], min(off + (i + 1) * a.bm[q], end), 0);
+            const int rows = end - off;
+            for (int i = 0; i < cnt; ++i) {
+                const int r0 = a.split[q] ? (int)((int64_t)i * rows / t[q]) : i * a.bm[q];
+                const int r1 = a.split[q] ? (int)((int64_t)(i + 1) * rows / t[q]) : min((i + 1) * a.bm[q], rows);
+                a.tiles[q][base + i] = make_int4(e, off + r0, off + r1, 0);
+            }
             for (int j = valid + threadIdx.x; j < nm; j += 1024) a.tiles[q][j] = make_int4(-1, 0, 0, 0);
             if (a.queue[q] && threadIdx.x < kQueueInts) a.queue[q][threadIdx.x] = 0;
         }
@@ -269,6 +276,13 @@ static void launch_pp_streamk(const GemmParams &p0, hipStream_t stream) {
     grouped_gemm_pp_streamk_kernel<BM, BN, BK, STAGES><<<device_cus(), 512, 0, stream>>>(p);
 }
 
+// From this many mean rows per expert the 256-row gate+up tiles run the
+// plain loop with a 3-deep weight ring; below it, the short-tile form, and
+// each expert's rows are shared evenly over its tiles (tiles of one expert
+// then take about the same time, so those sharing a weight panel stay in
+// step; measured on GPT-OSS: gate+up 1339 -> 1315-1323 us).
+constexpr int64_t kUpPlainRows = 768;
+
 // avg = mean rows per expert. Where it is below the tile height (experts of
 // ~100-190 rows under 192-row tiles) most tiles are short, so those launches
 // skip the MFMAs and row loads of missing rows.
@@ -284,7 +298,7 @@ static void launch_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t st
                 // sharing a weight panel in step (half the HBM re-reads), and
                 // its weight ring is 3 deep (two k-steps of weights in flight,
                 // the LDS full at 160 KB)
-                if (avg < 768) launch_pp_persistent<256, 128, MODE, 64, 2, 2, true>(p, stream);
+                if (avg < kUpPlainRows) launch_pp_persistent<256, 128, MODE, 64, 2, 2, true>(p, stream);
                 else launch_pp_persistent<256, 128, MODE, 64, 3, 2>(p, stream);
                 break;
             case 192: launch_pp_persistent<192, 128, MODE, 64, 3, 2, true>(p, stream); break;
@@ -329,7 +343,8 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
 
     uint32_t *order_up = reinterpret_cast<uint32_t *>(ws + pl.order_up_off);
     uint32_t *order_down = reinterpret_cast<uint32_t *>(ws + pl.order_down_off);
-    TileTableArgs ta;
+    const int64_t avg = (int64_t)N / E;
+    TileTableArgs ta{};
     ta.bm[0] = pl.bm_up;
     ta.bm[1] = pl.bm_down;
     ta.n_mtiles[0] = pl.n_mtiles_up;
@@ -347,6 +362,7 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     int *queue_up = reinterpret_cast<int *>(ws + pl.queue_off);
     ta.queue[0] = queue_up;
     ta.queue[1] = nullptr;
+    ta.split[0] = (pl.bm_up == 256 && avg < kUpPlainRows);
     launch_tile_table(expert_offsets, E, N, ta, stream);
     if (atomic) {
         prof_begin(stream, kKAccZero);
@@ -376,8 +392,8 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.K = D;
     p.valid_mtiles = valid_counts;
     p.queue = queue_up;
-    if (saved) launch_gemm<kGateUpSave>(pl.bm_up, (int64_t)N / E, p, stream);
-    else launch_gemm<kGateUp>(pl.bm_up, (int64_t)N / E, p, stream);
+    if (saved) launch_gemm<kGateUpSave>(pl.bm_up, avg, p, stream);
+    else launch_gemm<kGateUp>(pl.bm_up, avg, p, stream);
 
     // down + scatter-add (atomic) or per-route rows: A = h (slot order), K = F, N = D
     p.tiles = tiles_down;
@@ -393,13 +409,13 @@ hipError_t launch_scatter_ffn(const uint16_t *x, const uint16_t *w1, const uint1
     p.N = D;
     p.K = F;
     if (atomic) {
-        launch_gemm<kDown>(pl.bm_down, (int64_t)N / E, p, stream);
+        launch_gemm<kDown>(pl.bm_down, avg, p, stream);
         prof_begin(stream, kKFinalize);
         acc_finalize_kernel<<<grid_for(n4, 256 * 4), 256, 0, stream>>>(reinterpret_cast<const float4 *>(acc),
                                                                         reinterpret_cast<uint2 *>(out), n4);
         prof_end(stream, kKFinalize);
     } else {
-        launch_gemm<kDownRows>(pl.bm_down, (int64_t)N / E, p, stream);
+        launch_gemm<kDownRows>(pl.bm_down, avg, p, stream);
         launch_combine_rows(acc, out, S, D, k, stream);
     }
     return hipGetLastError();

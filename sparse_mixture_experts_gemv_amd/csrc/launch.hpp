@@ -61,6 +61,9 @@ struct TileTableArgs {
     uint32_t *order[2];
     int *valid[2];  // number of non-empty M tiles
     int *queue[2];  // tile claim counters of the GEMM (kQueueInts ints) to zero, or NULL
+    // 0: an expert's tiles hold bm rows each and the last one the rest;
+    // 1: its ceil(rows / bm) tiles share the rows evenly (sizes differ by at most one)
+    int split[2];
 };
 // Tile claim counters of one dynamically scheduled GEMM: one per XCD, each on
 // its own 64-byte line.

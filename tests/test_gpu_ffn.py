@@ -116,6 +116,10 @@ ROW_EDGES = {
     # mean 225 rows per expert -> 256-row gate+up tiles (128-row down tiles):
     # the same edges around 256, 512 and a tail expert
     "256": (1800, 2, [1, 9, 16, 17, 33, 128, 160, 255, 256, 257, 300, 400, 512, 513, 600]),
+    # mean 720 rows per expert -> 256-row gate+up tiles with each expert's
+    # rows shared evenly over its tiles (129 + 128, 171 x 3, 192/192/192/193,
+    # 205 x 5, ...), 192-row down tiles
+    "256split": (3600, 2, [257, 383, 511, 513, 700, 767, 769, 1000, 1025]),
 }
 
 
