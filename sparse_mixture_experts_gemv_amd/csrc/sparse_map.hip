@@ -31,7 +31,6 @@
 namespace smoe {
 
 constexpr int kMaxExperts = 1024;
-constexpr int kMapUnroll = 4;  // groups of 64 routes whose ids are loaded together (small maps)
 
 __device__ __forceinline__ unsigned long long match_any(int key, int nbits) {
     unsigned long long m = __ballot(1);
@@ -98,12 +97,14 @@ __global__ __launch_bounds__(256) void smap_rowscan_kernel(int32_t *__restrict__
 // The whole map in one workgroup of 1024 threads, for maps of at most
 // kSmallMapRoutes routes (decode-sized batches), where the three launches
 // of the general path cost more than the work. Wave w takes the contiguous
-// chunk [w L, (w + 1) L) of routes, so a route's rank among the routes of its
-// expert is: earlier waves' counts of that expert, then earlier groups of 64
-// in its own wave, then lower lanes of its own group -- the same stable slot
-// as the general path.
+// chunk [w L, (w + 1) L) of routes (L a multiple of 64), so a route's rank
+// among the routes of its expert is: earlier waves' counts of that expert,
+// then earlier groups of 64 in its own wave, then lower lanes of its own
+// group -- the same stable slot as the general path. A lane loads its ids
+// once, all in one round, and keeps them for both passes.
 constexpr int kSmallMapRoutes = 8192;
 constexpr int kSmallMapWaves = 16;
+constexpr int kSmallPerLane = kSmallMapRoutes / (kSmallMapWaves * 64);  // groups of 64 per wave, at most
 
 __global__ __launch_bounds__(1024) void smap_small_kernel(const int32_t *__restrict__ ids, int N, int E, int nbits,
                                                           int L, int32_t *__restrict__ expert_counts,
@@ -113,22 +114,24 @@ __global__ __launch_bounds__(1024) void smap_small_kernel(const int32_t *__restr
     __shared__ int32_t s_cnt[kSmallMapWaves * kMaxExperts];  // [wave][expert]: count, then base
     __shared__ int s_tmp[kSmallMapWaves];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int base = w * L;
+    // route base + 64 j + lane, or the sentinel E past the wave's chunk, past N or out of range
+    int ev[kSmallPerLane];
+#pragma unroll
+    for (int j = 0; j < kSmallPerLane; ++j) {
+        const int f = base + 64 * j + lane;
+        int e = (64 * j < L && f < N) ? ids[f] : E;
+        if ((unsigned)e >= (unsigned)E) e = E;
+        ev[j] = e;
+    }
     int32_t *my = s_cnt + w * E;
     for (int e = lane; e < E; e += 64) my[e] = 0;
-    const int base = w * L;
     const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     // pass 1: per-wave counts (only a group's lowest lane of an expert writes)
-    for (int g0 = 0; g0 < L; g0 += 64 * kMapUnroll) {
-        int ev[kMapUnroll];
 #pragma unroll
-        for (int u = 0; u < kMapUnroll; ++u) {
-            const int f = base + g0 + 64 * u + lane;
-            ev[u] = f < N ? ids[f] : E;
-        }
-#pragma unroll
-        for (int u = 0; u < kMapUnroll; ++u) {
-            int e = ev[u];
-            if ((unsigned)e >= (unsigned)E) e = E;
+    for (int j = 0; j < kSmallPerLane; ++j) {
+        if (64 * j < L) {
+            const int e = ev[j];
             const unsigned long long m = match_any(e, nbits);
             const int leader = __ffsll(m) - 1;
             if (lane == leader && e < E) my[e] += __popcll(m);
@@ -168,18 +171,11 @@ __global__ __launch_bounds__(1024) void smap_small_kernel(const int32_t *__restr
     if (e == 0) expert_offsets[E] = total;
     __syncthreads();
     // pass 2: slots
-    for (int g0 = 0; g0 < L; g0 += 64 * kMapUnroll) {
-        int ev[kMapUnroll];
 #pragma unroll
-        for (int u = 0; u < kMapUnroll; ++u) {
-            const int f = base + g0 + 64 * u + lane;
-            ev[u] = f < N ? ids[f] : E;
-        }
-#pragma unroll
-        for (int u = 0; u < kMapUnroll; ++u) {
-            const int f = base + g0 + 64 * u + lane;
-            int ex = ev[u];
-            if ((unsigned)ex >= (unsigned)E) ex = E;
+    for (int j = 0; j < kSmallPerLane; ++j) {
+        if (64 * j < L) {
+            const int f = base + 64 * j + lane;
+            const int ex = ev[j];
             const unsigned long long m = match_any(ex, nbits);
             const int leader = __ffsll(m) - 1;
             int b = (lane == leader && ex < E) ? my[ex] : 0;
@@ -470,9 +466,8 @@ hipError_t launch_sparse_map(const int32_t *ids, int N, int E, int32_t *expert_c
         return hipGetLastError();
     }
     if (N <= kSmallMapRoutes) {
-        // chunks of whole 64 * kMapUnroll groups, one per wave
-        constexpr int G = 64 * kMapUnroll;
-        const int L = ((N + kSmallMapWaves - 1) / kSmallMapWaves + G - 1) / G * G;
+        // chunks of whole groups of 64 routes, one per wave (L <= 64 * kSmallPerLane)
+        const int L = ((N + kSmallMapWaves - 1) / kSmallMapWaves + 63) / 64 * 64;
         prof_begin(stream, kKMapSmall);
         const int sbits = 32 - __builtin_clz((unsigned)E);  // bits to hold 0..E (E is the sentinel)
         smap_small_kernel<<<1, 1024, 0, stream>>>(ids, N, E, sbits, L, expert_counts, expert_offsets, sparse_rows,
