@@ -8,7 +8,7 @@
 // itself (contiguous A) or the token of the slot (gathered A: token rows of
 // X read in place, never copied).
 //
-// Four epilogues:
+// The epilogues (MODE):
 //   kGateUp   two B matrices (W1, W3) share every A tile; the tile writes
 //             h = bf16(SiLU(A W1) * (A W3)) in slot order (fused gate+up).
 //   kDown     one B matrix (W2); the tile scales each row by its route's

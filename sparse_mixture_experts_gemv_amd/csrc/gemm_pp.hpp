@@ -19,12 +19,13 @@
 // of each per SIMD), running the same sequence "read fragments of step k
 // from LDS | barrier | MFMAs of step k | barrier" one barrier phase apart,
 // so on every SIMD one wave feeds the matrix core while the other reads LDS.
-// The LDS holds a ring of STAGES steps. At the start of its read phase for
-// step k, group 0 issues the DMA of step k + STAGES - 1 into the slot of
-// step k - 1 (both groups finished reading it one phase earlier), so
-// STAGES - 1 steps of operands are in flight per CU; at the end of its MFMA
-// phase it waits until step k + 1 has landed, before the barrier that opens
-// step k + 1 to readers. The DMA is plain assembly with explicit vmcnt
+// The LDS holds two rings: STAGES steps of B and STAGES_A steps of A. At the
+// start of its read phase for step k, group 0 issues the DMA of step
+// k + STAGES_A - 1 of A and of step k + STAGES - 1 of B, each into the slot
+// of step k - 1 of its ring (both groups finished reading it one phase
+// earlier), so up to STAGES - 1 steps of weights are in flight per CU; at
+// the end of its MFMA phase it waits until step k + 1 has landed, before
+// the barrier that opens step k + 1 to readers. The DMA is plain assembly with explicit vmcnt
 // bookkeeping because the compiler would drain every DMA before each LDS
 // read (it cannot prove the ring slots disjoint).
 #pragma once

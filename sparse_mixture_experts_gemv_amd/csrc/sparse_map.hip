@@ -11,16 +11,19 @@
 // Unlike that pull request's atomic slot claim, the assignment here is a
 // stable rank, so the map is identical on every run.
 //
-// Layout of the work: routes are taken 64 at a time by a wavefront. Within a
-// group of 64, a lane finds the lanes holding the same expert with one ballot
-// per id bit (match-any), so its rank among them is a popcount and the
-// group's count per expert is known to the lowest such lane, which updates a
-// per-wave LDS counter. No global atomics are used anywhere. Large maps:
-//   pass 1 (hist):    per chunk of routes, counts -> cnt[e][chunk] (workspace)
+// Layout of the work: routes are taken 64 at a time by a wavefront; a lane's
+// rank among the lanes of its group holding the same expert is a popcount of
+// their lane mask, and the group's count per expert goes to a per-wave LDS
+// counter. No global atomics are used anywhere. Large maps:
+//   pass 1 (hist):    per chunk of routes, counts by LDS atomic adds (the
+//                     sum does not depend on their order) -> cnt[e][chunk]
 //   pass 2 (rowscan): per expert, exclusive scan over chunks, total
 //   pass 3 (assign):  offsets from the totals, then per chunk a local stable
-//                     sort by expert in LDS -> slots, written out in runs
-// Small maps (at most 8192 routes) take all three steps in one workgroup.
+//                     sort by expert in LDS (lane masks built by OR-ing each
+//                     lane's bit into one LDS word per wave and expert) ->
+//                     slots, written out in runs
+// Small maps (at most 8192 routes) take all three steps in one workgroup,
+// with the lane masks from one ballot per id bit (match-any).
 #include <algorithm>
 #include <mutex>
 
