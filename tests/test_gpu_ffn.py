@@ -97,6 +97,23 @@ def test_ffn_uneven_tiles_all_tokens(oracle_lib, S, E, skew):
 
 
 @pytest.mark.parametrize("atomic", [False, True], ids=["rows", "atomic"])
+@pytest.mark.parametrize("S,D,F,skew", [(300, 128, 192, None), (12288, 64, 128, None), (4000, 64, 192, 1.2)])
+def test_ffn_max_experts_all_tokens(oracle_lib, S, D, F, skew, atomic):
+    """The largest expert count the library takes (E = 1024) with k = 16:
+    mostly empty experts at S = 300 (32-row tiles); 192 rows per expert at
+    S = 12288 (256-row gate+up tiles with the rows split evenly, 128-row down
+    tiles); Zipf-skewed load, one tile table thread per expert throughout."""
+    E, k = 1024, 16
+    cfg = wl.MoEConfig("maxe", 63, S, D, F, E, k, None)
+    p = make_problem(cfg)
+    ids = wl.gen_random_ids(S, k, E, seed=S + 7, skew=skew)
+    w = np.random.default_rng(S).dirichlet(np.ones(k), size=S).astype(np.float32)
+    got = gpu_ffn(p, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), atomic)
+    ref = oracle_ffn_rows(oracle_lib, p, ids, w, np.arange(S))
+    assert_close(got, ref, f"E=1024 k=16 S={S} skew={skew} {'atomic' if atomic else 'rows'}", configured=False)
+
+
+@pytest.mark.parametrize("atomic", [False, True], ids=["rows", "atomic"])
 def test_ffn_skewed_single_expert(oracle_lib, atomic):
     """All routes on two experts: one expert spans many M tiles, the rest are empty."""
     cfg = wl.MoEConfig("skew", 61, 700, 128, 192, 16, 2, None)
