@@ -37,6 +37,7 @@ SMALL = [  # (S, D, F, E, k, skew): recompute tile from S*k/E (256/192/64/32), d
     (200, 128, 256, 16, 2, 1.2),    # 25: 32 / 32, skewed
     (40, 256, 128, 64, 8, None),    # 5: most experts empty
     (33, 320, 192, 4, 1, None),     # k = 1
+    (300, 64, 128, 1024, 16, None),  # E = 1024, k = 16: the largest expert count, most experts with 0-10 rows
 ]
 ROW_L2_BAR = 2e-2
 MAXREL_BAR = 2e-2

@@ -28,6 +28,7 @@ SHAPES = [  # (S, k, D_in, D_out, E, skew)
     (65, 1, 64, 64, 4, None),      # k = 1
     (40, 4, 128, 256, 64, None),   # 2.5 rows per expert: most experts empty
     (30, 20, 64, 128, 24, None),   # k = 20: the finalize pass takes the routes in two chunks
+    (300, 16, 64, 128, 1024, None),  # E = 1024, k = 16: ~5 rows per expert, the largest expert count
 ]
 
 
