@@ -108,6 +108,7 @@ __global__ __launch_bounds__(256) void smap_rowscan_kernel(int32_t *__restrict__
 constexpr int kSmallMapRoutes = 8192;
 constexpr int kSmallMapWaves = 16;
 constexpr int kSmallPerLane = kSmallMapRoutes / (kSmallMapWaves * 64);  // groups of 64 per wave, at most
+static_assert(kSmallMapRoutes % (kSmallMapWaves * 64) == 0, "a wave's chunk of at most kSmallMapRoutes / 16 routes fits kSmallPerLane groups");
 
 __global__ __launch_bounds__(1024) void smap_small_kernel(const int32_t *__restrict__ ids, int N, int E, int nbits,
                                                           int L, int32_t *__restrict__ expert_counts,
