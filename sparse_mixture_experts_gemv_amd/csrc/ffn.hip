@@ -29,13 +29,13 @@ namespace smoe {
 // writes its (expert, row_begin, row_end) entries: bm rows per tile and the
 // rest in the last, or (split) the rows shared evenly over the same number
 // of tiles, so that no tile of the expert is much shorter than the others.
-// The block order is then
-// filled by the threads of every workgroup, each workgroup having formed the
-// same T_e: blocks [T_e * nn, (T_e + c_e) * nn) belong to expert e (c_e its
-// tile count, nn the N tiles), N tile major, the expert's M tiles minor; a
-// thread finds the expert of a block by binary search over T_e. Two GEMMs
-// (tile heights) are handled in one launch. Entries past the real tile count
-// are marked empty (expert = -1, order M field all ones).
+// The block order is then filled by the threads of every workgroup, each
+// workgroup having formed the same T_e: blocks [T_e * nn, (T_e + c_e) * nn)
+// belong to expert e (c_e its tile count, nn the N tiles), N tile major, the
+// expert's M tiles minor; a thread finds the expert of a block by binary
+// search over T_e. Two GEMMs (tile heights) are handled in one launch.
+// Entries past the real tile count are marked empty (expert = -1, order M
+// field all ones).
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t *__restrict__ offsets, int E, int N,
                                                           const TileTableArgs a) {
     __shared__ int s_wave[2][16];
