@@ -135,12 +135,15 @@ static void bwd_tile(const GemmParams &p0, hipStream_t stream) {
 }
 
 // gate+up recomputation: the tile shapes of the forward gate+up GEMM, with
-// its 3-deep weight ring from ~770 rows per expert
+// its 3-deep weight ring; below ~770 rows per expert, as in the forward, the
+// short-tile form over evenly split tiles (GPT-OSS recomputation 1469-1497
+// -> 1352-1375 us, Qwen2 S = 4096 1288-1338 -> 1233-1274 us against the
+// plain 2-deep form)
 static void launch_recompute(int bm, int64_t avg, const GemmParams &p, hipStream_t stream) {
     switch (bm) {
         case 256:
             if (avg >= 768) bwd_tile<256, 128, kGateUpSave, 64, 3, 2, false, 0>(p, stream);
-            else bwd_tile<256, 128, kGateUpSave, 64, 2, 2, false, 0>(p, stream);
+            else bwd_tile<256, 128, kGateUpSave, 64, 3, 2, true, 0>(p, stream);
             break;
         case 192: bwd_tile<192, 128, kGateUpSave, 64, 3, 2, true, 0>(p, stream); break;
         case 64: bwd_tile<64, 128, kGateUpSave, 64, 3, 3, false, 0>(p, stream); break;
@@ -196,6 +199,7 @@ hipError_t launch_ffn_bwd(const uint16_t *x, const uint16_t *w1, const uint16_t 
     ta.tiles[1] = tiles_b;
     ta.order[1] = reinterpret_cast<uint32_t *>(ws + pl.order_h);
     ta.valid[1] = counts + 1;
+    ta.split[0] = (pl.bm_r == 256 && (int64_t)N / std::max(E, 1) < 768);  // as the forward's short-tile launches
     launch_tile_table(expert_offsets, E, N, ta, stream);
     TileTableArgs tx{};
     tx.bm[0] = tx.bm[1] = pl.bm_x;
