@@ -19,16 +19,21 @@
 // of each per SIMD), running the same sequence "read fragments of step k
 // from LDS | barrier | MFMAs of step k | barrier" one barrier phase apart,
 // so on every SIMD one wave feeds the matrix core while the other reads LDS.
-// The LDS holds two rings: STAGES steps of B and STAGES_A steps of A. At the
-// start of its read phase for step k, group 0 issues the DMA of step
-// k + STAGES_A - 1 of A and of step k + STAGES - 1 of B, each into the slot
-// of step k - 1 of its ring (both groups finished reading it one phase
-// earlier), so up to STAGES - 1 steps of weights are in flight per CU; at
-// the end of its MFMA phase it waits until step k + 1 has landed, before
-// the barrier that opens step k + 1 to readers. The DMA is plain assembly with explicit vmcnt
-// bookkeeping because the compiler would drain every DMA before each LDS
-// read (it cannot prove the ring slots disjoint).
+// The LDS holds two rings: STAGES steps of B and STAGES_A steps of A. During
+// its read phase for step k, a group issues the DMA of step k + STAGES_A - 1
+// of A and/or of step k + STAGES - 1 of B, each into the slot of step k - 1
+// of its ring (both groups finished reading it at least one phase earlier),
+// spread among its fragment reads, so up to STAGES - 1 steps of weights are
+// in flight per CU. Either group 0 issues both rings and, at the end of its
+// MFMA phase, waits until step k + 1 has landed; or (the gate+up tiles)
+// group 0 issues A and waits for it there, and group 1 issues B and waits,
+// at the end of its read phase, for the B of step k + 1. Both waits come
+// before the barrier that opens step k + 1 to readers. The DMA is plain
+// assembly with explicit vmcnt bookkeeping because the compiler would drain
+// every DMA before each LDS read (it cannot prove the ring slots disjoint).
 #pragma once
+
+#include <type_traits>
 
 #include "gemm.hpp"
 
@@ -108,6 +113,14 @@ struct PPGeom {
         (MODE == kGateUp || MODE == kGateUpSave || MODE == kLinBf16) ? BM * (BN + 8) * 2 : 0;
     static constexpr int SMEM = RING > STAGE_BF16 ? RING : STAGE_BF16;
 };
+
+// Whether the two wave groups share the DMA issue (group 0 the token rows,
+// group 1 the weights, each in its own read phase) rather than group 0
+// issuing both. Measured against group 0 alone (both with the instructions
+// spread among the reads): the gate+up GEMM 1524 -> 1490 us on Mixtral, 1245
+// -> 1198 us on GPT-OSS, 1111 -> 1083 us on Qwen2 S = 4096; the down GEMM 1-3 %
+// slower on the same shapes, so only the two-weight tiles share.
+constexpr bool pp_dma_split(int mode) { return mode == kGateUp || mode == kGateUpSave; }
 
 // One tile (mt, nt), k-steps [k_begin, k_end) of BK, epilogue included. All
 // 512 threads of the workgroup call it together; on return every LDS read of
@@ -208,6 +221,10 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
     const pp_i32x4 b_rsrc0 = pp_desc(p.B0 + b_off, b_bytes);
     const pp_i32x4 b_rsrc1 = pp_desc((NB == 2 || KSPLIT ? p.B1 : p.B0) + b_off, b_bytes);
     const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+    // Who issues the DMA (measured per epilogue, see pp_dma_split): with SPLIT,
+    // group 0 the A (token row) DMA and group 1 the B (weight) DMA, each
+    // during its own read phase; otherwise group 0 issues both.
+    constexpr bool SPLIT = pp_dma_split(MODE);
     uint32_t a_voff[A_PER_WAVE], b_voff[B_PER_WAVE];
     if (group == 0) {
 #pragma unroll
@@ -220,6 +237,8 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
             const uint32_t arow = gather ? (uint32_t)(p.slot_src[slot] / p.topk) : (uint32_t)(slot - row0);
             a_voff[i] = arow * (uint32_t)K * 2u + (uint32_t)c * 16u;
         }
+    }
+    if (group == (SPLIT ? 1 : 0)) {
 #pragma unroll
         for (int i = 0; i < B_PER_WAVE; ++i) {
             const int j = wl + 4 * i;
@@ -304,7 +323,21 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
     const int KT = k_end;
 #define SMOE_SLOT_A(KT_) (((KT_) - k_begin) % STAGES_A)
 #define SMOE_SLOT_B(KT_) (((KT_) - k_begin) % STAGES)
-    if (group == 0) {
+    if (SPLIT) {
+        if (group == 0) {
+#pragma unroll
+            for (int st = 0; st < STAGES_A - 1; ++st)
+                if (k_begin + st < KT) SMOE_PP_ISSUE_A(k_begin + st);
+            if (KT - k_begin >= STAGES_A - 1) pp_wait_dma<(STAGES_A - 2) * A_PER_WAVE>();  // first step landed
+            else pp_wait_dma<0>();
+        } else {
+#pragma unroll
+            for (int st = 0; st < STAGES - 1; ++st)
+                if (k_begin + st < KT) SMOE_PP_ISSUE_B(k_begin + st);
+            if (KT - k_begin >= STAGES - 1) pp_wait_dma<(STAGES - 2) * B_PER_WAVE>();
+            else pp_wait_dma<0>();
+        }
+    } else if (group == 0) {
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st) {
             if (st < STAGES_A - 1 && k_begin + st < KT) SMOE_PP_ISSUE_A(k_begin + st);
@@ -318,10 +351,6 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
 
     for (int kt = k_begin; kt < KT; ++kt) {
         // ---- read phase: refill the slots of step kt-1, then read step kt ----
-        if (group == 0) {
-            if (kt + STAGES_A - 1 < KT) SMOE_PP_ISSUE_A(kt + STAGES_A - 1);
-            if (kt + STAGES - 1 < KT) SMOE_PP_ISSUE_B(kt + STAGES - 1);
-        }
         const char *sa = smem + SMOE_SLOT_A(kt) * A_BYTES;
         const char *sb = smem + B_RING + SMOE_SLOT_B(kt) * (NB * B_BYTES);
         // one register per fragment column block holds slot base + lane
@@ -340,26 +369,97 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
         }
         uint4 af[KK][MT];
         uint4 bf[KK][NB][NT];
+        // DMA instruction d of step kt's refill: d < A_PER_WAVE the A ring's
+        // instruction d, else the B ring's instruction d - A_PER_WAVE (A
+        // before B: the order the vmcnt targets assume). Only in steady state,
+        // when this wave's ring(s) are refilled at all.
+        auto dma_one = [&](const int d) {
+            if (d < A_PER_WAVE) {
+                const int ia = d < A_PER_WAVE ? d : 0;
+                if (!SKIP_A || ia < a_cnt)
+                    pp_dma16(a_rsrc, smem_addr + SMOE_SLOT_A(kt + STAGES_A - 1) * A_BYTES + (wl + 4 * ia) * 1024,
+                             a_voff[ia], (uint32_t)(kt + STAGES_A - 1) * (BK * 2));
+            } else if (d < DMA_PER_WAVE) {
+                const int ib = (d >= A_PER_WAVE && d < DMA_PER_WAVE) ? d - A_PER_WAVE : 0;
+                const int ktb = kt + STAGES - 1;
+                const int jb = wl + 4 * ib;
+                const bool hi = KSPLIT && ktb * BK >= KB;
+                const uint32_t b_soff = (uint32_t)(ktb - (hi ? KB / BK : 0)) * (BT ? BK * 2u : BK * ldb);
+                pp_dma16(((jb / B_INSTR_PER_MAT) == 1 || hi) ? b_rsrc1 : b_rsrc0,
+                         smem_addr + B_RING + SMOE_SLOT_B(ktb) * (NB * B_BYTES) + jb * 1024, b_voff[ib], b_soff);
+            }
+        };
+        // The fragment reads of step kt, with the DMA instructions d0 ..
+        // d0 + ND - 1 of the refill spread among them: instruction d0 + i
+        // follows read (i + 1) RP - 1. A wave that issues a run of DMA
+        // instructions stalls until the CU's vector memory unit has taken them
+        // (about 16 cycles per 1 KB instruction), so issued all at once, as
+        // before the reads, they delay every read behind them; spread, the
+        // reads and the DMA proceed together.
+        constexpr int PER_KK = MT + NB * NT * (BT ? 1 : 2);
+        constexpr int READS = KK * PER_KK;
+        auto reads = [&](auto d0_tag, auto nd_tag) {
+            constexpr int D0 = decltype(d0_tag)::value, ND = decltype(nd_tag)::value;
+            constexpr int RP = (ND > 0 && READS >= ND) ? READS / (ND > 0 ? ND : 1) : 1;
+            auto hook = [&](const int r) {
+                if (ND > 0 && (r % RP) == RP - 1 && r / RP < ND) dma_one(D0 + r / RP);
+            };
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+            for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-            for (int i = 0; i < MT; ++i) af[kk][i] = *reinterpret_cast<const uint4 *>(sa + a_rd[kk] + i * A_RD_I);
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    if constexpr (BT) {
-                        bf[kk][b][j] = *reinterpret_cast<const uint4 *>(sb + b * B_BYTES + b_rd[kk] + j * B_RD_J);
-                    } else {
-                        const char *bp = smem + b_lane[j] + b * B_BYTES + kk * B_RD_KK;
-                        const uint2 lo = pp_tr(bp);
-                        const uint2 hi = pp_tr(bp + B_RD_H);
-                        bf[kk][b][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    }
+                for (int i = 0; i < MT; ++i) {
+                    af[kk][i] = *reinterpret_cast<const uint4 *>(sa + a_rd[kk] + i * A_RD_I);
+                    hook(kk * PER_KK + i);
                 }
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) {
+                        if constexpr (BT) {
+                            bf[kk][b][j] = *reinterpret_cast<const uint4 *>(sb + b * B_BYTES + b_rd[kk] + j * B_RD_J);
+                            hook(kk * PER_KK + MT + b * NT + j);
+                        } else {
+                            const char *bp = smem + b_lane[j] + b * B_BYTES + kk * B_RD_KK;
+                            const uint2 lo = pp_tr(bp);
+                            hook(kk * PER_KK + MT + 2 * (b * NT + j));
+                            const uint2 hi = pp_tr(bp + B_RD_H);
+                            hook(kk * PER_KK + MT + 2 * (b * NT + j) + 1);
+                            bf[kk][b][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                        }
+                    }
+            }
+#pragma unroll
+            for (int d = READS / RP; d < ND; ++d) dma_one(D0 + d);
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using IA = std::integral_constant<int, A_PER_WAVE>;
+        using IB = std::integral_constant<int, B_PER_WAVE>;
+        using ID = std::integral_constant<int, DMA_PER_WAVE>;
+        if constexpr (SPLIT) {
+            if (group == 0) {
+                if (kt + STAGES_A - 1 < KT) reads(I0{}, IA{});
+                else reads(I0{}, I0{});
+            } else {
+                if (kt + STAGES - 1 < KT) reads(IA{}, IB{});
+                else reads(I0{}, I0{});
+            }
+        } else if (group == 0 && kt + STAGES - 1 < KT) {  // steady state: both rings refilled
+            reads(I0{}, ID{});
+        } else {
+            // the last steps: the refills still due (the A ring's, when it is
+            // shallower than the B ring), then the reads
+            if (group == 0) {
+                if (kt + STAGES_A - 1 < KT) SMOE_PP_ISSUE_A(kt + STAGES_A - 1);
+                if (kt + STAGES - 1 < KT) SMOE_PP_ISSUE_B(kt + STAGES - 1);
+            }
+            reads(I0{}, I0{});
         }
         // reads complete before the barrier: after it the slots may be refilled
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (SPLIT && group == 1) {  // B of step kt+1 must have landed before the barrier that opens it
+            if (kt + STAGES - 1 < KT) pp_wait_dma<(STAGES - 2) * B_PER_WAVE>();
+            else pp_wait_dma<0>();
+        }
         pp_barrier();
         // ---- MFMA phase ----
         __builtin_amdgcn_s_setprio(1);
@@ -390,7 +490,10 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        if (group == 0) {  // step kt+1 must have landed before the barrier that opens it
+        if (SPLIT && group == 0) {  // A of step kt+1 must have landed before the barrier that opens it
+            if (kt + STAGES_A - 1 < KT) pp_wait_dma<(STAGES_A - 2) * A_PER_WAVE>();
+            else pp_wait_dma<0>();
+        } else if (group == 0) {  // step kt+1 must have landed before the barrier that opens it
             if (kt + STAGES - 1 < KT) pp_wait_dma<WAIT_STEADY>();
             else pp_wait_dma<0>();
         }
