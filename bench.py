@@ -471,6 +471,74 @@ def bench_map_sweep(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_route(args):
+    """The router alone (moe_route_topk) on the three routed workloads, beside the
+    cost of a plain read of the same token rows and of the split partial logits
+    (a library reduction over the tensor), each timed as a HIP graph of 20 calls
+    so that no host gap is counted."""
+    import torch
+
+    import sparse_mixture_experts_gemv_amd as smoe
+    from workloads import CONFIGS
+
+    def graph_us(fn, reps=20, replays=10):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / reps)
+        return sorted(times)[len(times) // 2]
+
+    rows = []
+    for name in ("mixtral", "gptoss", "dsv3"):
+        cfg = CONFIGS[name]
+        S, D, E, k = cfg.S, cfg.D, cfg.E, cfg.k
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        x = torch.randn((S, D), generator=gen, device="cuda").to(torch.bfloat16)
+        wg = (torch.randn((D, E), generator=gen, device="cuda") * D ** -0.5).to(torch.bfloat16)
+        ids = torch.empty((S, k), dtype=torch.int32, device="cuda")
+        wts = torch.empty((S, k), dtype=torch.float32, device="cuda")
+        wsb = smoe.route_workspace_bytes(S, E)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+        route_us = graph_us(lambda: smoe.moe_route_topk(x, wg, k, ids, wts, ws))
+        read_x_us = graph_us(lambda: x.sum(dtype=torch.float32))
+        smoe.profile_start(256)
+        for _ in range(20):
+            smoe.moe_route_topk(x, wg, k, ids, wts, ws)
+        kern = smoe.profile_stop()
+        row = {"workload": name, "S": S, "D": D, "E": E, "k": k, "route_us": round(route_us, 2),
+               "kernels_us": {n: round(1e3 * tot / c, 2) for n, (tot, c) in kern.items()},
+               "read_x_us": round(read_x_us, 2), "x_MB": round(S * D * 2 / 1e6, 1)}
+        nbytes = S * D * 2.0 + D * E * 2.0 + S * k * 8.0
+        row["algorithmic_MB"] = round(nbytes / 1e6, 1)
+        row["hbm_frac"] = round(nbytes / route_us / 1e3 / PEAK_HBM_GBS, 4)
+        row["read_x_hbm_frac"] = round(S * D * 2.0 / read_x_us / 1e3 / PEAK_HBM_GBS, 4)
+        if wsb:
+            part = torch.randn(wsb // 4, generator=gen, device="cuda")
+            row["read_partials_us"] = round(graph_us(lambda: part.sum()), 2)
+            row["partials_MB"] = round(wsb / 1e6, 1)
+        rows.append(row)
+        print(f"bench: route {name}: {row}", file=sys.stderr, flush=True)
+        del x, wg, ws
+    rec = {"metric": "router (logits, top-k, softmax) against a plain read of its input",
+           "value": rows[0]["hbm_frac"], "unit": "fraction of 8 TB/s (mixtral)", "n_gpus": 1,
+           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "router alone on the mixtral, gptoss and dsv3 shapes"}, "rows": rows}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,7 +548,7 @@ def main():
     ap.add_argument("--S", type=int, default=None, help="token count (default: the configuration's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "train", "pl_fwd", "pl_bwd", "map_sweep"],
+    ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "train", "pl_fwd", "pl_bwd", "map_sweep", "route"],
                     help="layer: the MoE forward (default); ffn_bwd: the expert FFN backward; "
                          "pl_fwd / pl_bwd: ParallelLinear up-projection")
     ap.add_argument("--dw-bf16", action="store_true",
@@ -519,6 +587,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n * 4, "launches": 3}))
+        return
+    if args.op == "route":
+        bench_route(args)
         return
     if args.op == "map_sweep":
         bench_map_sweep(args)
