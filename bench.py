@@ -539,6 +539,69 @@ def bench_route(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_vendor_gemm(args):
+    """Context for the GEMM rooflines: the vendor library's dense bf16 GEMM (torch.matmul,
+    contiguous 2-D operands) on the shapes of the Mixtral layer's two expert GEMMs, as one
+    dense product over all S*k routed rows and as a loop of per-expert products of S*k/E
+    rows. No gather, no SwiGLU, no weighted rows: a reference point, not the method."""
+    import torch
+
+    from workloads import CONFIGS
+
+    cfg = CONFIGS["mixtral"]
+    S, D, F, E, k = cfg.S, cfg.D, cfg.F, cfg.E, cfg.k
+    M = S * k
+    gen = torch.Generator(device="cuda").manual_seed(11)
+
+    def timed_us(fn, reps=10, rounds=10):
+        # each call is hundreds of microseconds of GPU work, far above the host's
+        # launch cost, so back-to-back eager calls keep the GPU busy
+        t_end = time.time() + 0.5  # settle the clock under load
+        while time.time() < t_end:
+            fn()
+            torch.cuda.synchronize()
+        times = []
+        for _ in range(rounds):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / reps)
+        return sorted(times)[len(times) // 2]
+
+    rows = []
+    for name, K, N in (("gate+up (W1 and W3 side by side)", D, 2 * F), ("down", F, D)):
+        a = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+        w = (torch.randn((K, N), generator=gen, device="cuda") * K ** -0.5).to(torch.bfloat16)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        flops = 2.0 * M * K * N
+        dense_us = timed_us(lambda: torch.matmul(a, w, out=c))
+        me = M // E
+        a_e = [a[e * me:(e + 1) * me] for e in range(E)]
+        c_e = [c[e * me:(e + 1) * me] for e in range(E)]
+        w_e = [w] * E  # the same weights for every expert: a loop of E products of M / E rows
+
+        def loop():
+            for e in range(E):
+                torch.matmul(a_e[e], w_e[e], out=c_e[e])
+
+        loop_us = timed_us(loop)
+        row = {"gemm": name, "M": M, "K": K, "N": N, "TFLOP": round(flops / 1e12, 4),
+               "dense_us": round(dense_us, 1), "dense_tflops": round(flops / dense_us / 1e6, 1),
+               "dense_frac": round(flops / dense_us / 1e6 / PEAK_BF16_TFLOPS, 4),
+               "per_expert_loop_us": round(loop_us, 1), "per_expert_loop_tflops": round(flops / loop_us / 1e6, 1)}
+        rows.append(row)
+        print(f"bench: vendor gemm {row}", file=sys.stderr, flush=True)
+        del a, w, c, a_e, c_e
+    rec = {"metric": "vendor dense bf16 GEMM on the Mixtral expert-GEMM shapes (context)",
+           "value": rows[0]["dense_tflops"], "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "torch.matmul on [S*k, K] x [K, N], mixtral shapes"}, "rows": rows}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -548,7 +611,7 @@ def main():
     ap.add_argument("--S", type=int, default=None, help="token count (default: the configuration's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "train", "pl_fwd", "pl_bwd", "map_sweep", "route"],
+    ap.add_argument("--op", default="layer", choices=["layer", "ffn_bwd", "train", "pl_fwd", "pl_bwd", "map_sweep", "route", "vendor_gemm"],
                     help="layer: the MoE forward (default); ffn_bwd: the expert FFN backward; "
                          "pl_fwd / pl_bwd: ParallelLinear up-projection")
     ap.add_argument("--dw-bf16", action="store_true",
@@ -590,6 +653,9 @@ def main():
         return
     if args.op == "route":
         bench_route(args)
+        return
+    if args.op == "vendor_gemm":
+        bench_vendor_gemm(args)
         return
     if args.op == "map_sweep":
         bench_map_sweep(args)
