@@ -264,13 +264,13 @@ int device_cus() {
 // gate+up GEMM claims its tiles from the per-XCD queues; the down GEMM walks
 // the order statically (measured, the queue made it 1-3 % slower on the
 // five workloads, while the gate+up gained up to 3 %).
-template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool SKIP_ROWS = false>
+template <int BM, int BN, int MODE, int BK, int STAGES, int STAGES_A = STAGES, bool SKIP_ROWS = false, int FLAGS = 0>
 static void launch_pp_persistent(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
     p.n_ntiles = (p.N + BN - 1) / BN;
     if (p.n_mtiles * p.n_ntiles == 0) return;
     constexpr bool kQueue = (MODE == kGateUp || MODE == kGateUpSave);
-    grouped_gemm_pp_persistent_kernel<BM, BN, MODE, BK, STAGES, STAGES_A, SKIP_ROWS, 0, kQueue>
+    grouped_gemm_pp_persistent_kernel<BM, BN, MODE, BK, STAGES, STAGES_A, SKIP_ROWS, FLAGS, kQueue>
         <<<device_cus(), 512, 0, stream>>>(p);
 }
 
@@ -324,10 +324,13 @@ static void launch_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t st
     } else {
         switch (bm) {
             case 192:
-                // 32-deep k-steps in 4-deep rings: measured on Mixtral against
-                // 2 to 7 weight stages, the fastest (5/5 +5 %, 3/3 +4 %)
+                // 64-deep k-steps in a 3/2 ring with the two wave groups
+                // sharing the DMA issue: Mixtral 907-912 -> 858-863 us and
+                // Qwen2 S = 4096 766-769 -> 703-707 us against the 32-deep
+                // 4/4 tile (the fastest ring of that tile when group 0 alone
+                // issues the DMA: 2 to 7 weight stages measured)
                 if (avg < 192) launch_pp_persistent<192, 256, MODE, 64, 3, 2, true>(p, stream);
-                else launch_pp_persistent<192, 256, MODE, 32, 4>(p, stream);
+                else launch_pp_persistent<192, 256, MODE, 64, 3, 2, false, kFlagSplitDma>(p, stream);
                 break;
             case 128: launch_pp_persistent<128, 256, MODE, 64, 4, 2>(p, stream); break;
             case 64: launch_pp_persistent<64, 256, MODE, 64, 3>(p, stream); break;

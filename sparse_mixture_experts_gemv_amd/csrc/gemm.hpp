@@ -49,7 +49,8 @@
 namespace smoe {
 
 enum GemmMode { kGateUp = 0, kDown = 1, kLogits = 2, kDownRows = 3, kLinBf16 = 4, kGateUpSave = 5, kSwigluBwd = 6 };
-enum GemmFlags { kFlagBT = 1, kFlagKSplit = 2 };
+// kFlagSplitDma: the two wave groups share the DMA issue (see pp_dma_split)
+enum GemmFlags { kFlagBT = 1, kFlagKSplit = 2, kFlagSplitDma = 4 };
 
 struct GemmParams {
     const uint16_t *A;        // X [S, K] (kGateUp, kLogits) or h [S*k, K] (kDown, kDownRows)

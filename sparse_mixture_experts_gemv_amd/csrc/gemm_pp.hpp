@@ -118,9 +118,15 @@ struct PPGeom {
 // group 1 the weights, each in its own read phase) rather than group 0
 // issuing both. Measured against group 0 alone (both with the instructions
 // spread among the reads): the gate+up GEMM 1524 -> 1490 us on Mixtral, 1245
-// -> 1198 us on GPT-OSS, 1111 -> 1083 us on Qwen2 S = 4096; the down GEMM 1-3 %
-// slower on the same shapes, so only the two-weight tiles share.
-constexpr bool pp_dma_split(int mode) { return mode == kGateUp || mode == kGateUpSave; }
+// -> 1198 us on GPT-OSS, 1111 -> 1083 us on Qwen2 S = 4096. On the down GEMM's
+// 32-deep tiles sharing was 1-3 % slower, but on its 192 x 256 tile with
+// 64-deep k-steps (3/2 rings) it pays: Mixtral 885-888 -> 842-844 us,
+// Qwen2 S = 4096 748-762 -> 693-696 us, which beats the 32-deep 4/4 tile
+// without sharing; launches opt in with kFlagSplitDma (the 128-row and
+// short-tile down launches measured 0-1 % slower with it).
+constexpr bool pp_dma_split(int mode, int flags) {
+    return mode == kGateUp || mode == kGateUpSave || (flags & kFlagSplitDma) != 0;
+}
 
 // One tile (mt, nt), k-steps [k_begin, k_end) of BK, epilogue included. All
 // 512 threads of the workgroup call it together; on return every LDS read of
@@ -224,7 +230,7 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
     // Who issues the DMA (measured per epilogue, see pp_dma_split): with SPLIT,
     // group 0 the A (token row) DMA and group 1 the B (weight) DMA, each
     // during its own read phase; otherwise group 0 issues both.
-    constexpr bool SPLIT = pp_dma_split(MODE);
+    constexpr bool SPLIT = pp_dma_split(MODE, FLAGS);
     uint32_t a_voff[A_PER_WAVE], b_voff[B_PER_WAVE];
     if (group == 0) {
 #pragma unroll
