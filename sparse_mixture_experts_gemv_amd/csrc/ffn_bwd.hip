@@ -152,15 +152,20 @@ static void launch_recompute(int bm, int64_t avg, const GemmParams &p, hipStream
 }
 
 // one transposed weight, 256-column tiles (128 for 32-row tiles); 192-row
-// tiles over experts shorter than the tile take the short-tile path
+// tiles over experts shorter than the tile take the short-tile path. The
+// 192-row plain tiles and the 128-row tiles share the DMA issue between the
+// two wave groups (two alternating runs on one box: dx on Mixtral 1800-1803 ->
+// 1496-1510 us, Qwen2 S = 4096 1239-1263 -> 1156-1159 us; dh on Mixtral
+// 1156-1165 -> 1101-1103 us, Qwen2 843-860 -> 820-825 us, GPT-OSS 929-947 ->
+// 913-918 us; GPT-OSS dx unchanged)
 template <int MODE, int FLAGS>
 static void launch_bwd_bt(int bm, int64_t avg, const GemmParams &p, hipStream_t stream) {
     switch (bm) {
         case 192:
             if (avg < 192) bwd_tile<192, 256, MODE, 64, 3, 2, true, FLAGS>(p, stream);
-            else bwd_tile<192, 256, MODE, 64, 3, 2, false, FLAGS>(p, stream);
+            else bwd_tile<192, 256, MODE, 64, 3, 2, false, FLAGS | kFlagSplitDma>(p, stream);
             break;
-        case 128: bwd_tile<128, 256, MODE, 64, 4, 2, false, FLAGS>(p, stream); break;
+        case 128: bwd_tile<128, 256, MODE, 64, 4, 2, false, FLAGS | kFlagSplitDma>(p, stream); break;
         case 64: bwd_tile<64, 256, MODE, 64, 3, 3, false, FLAGS>(p, stream); break;
         default: bwd_tile<32, 128, MODE, 64, 4, 4, false, FLAGS>(p, stream); break;
     }

@@ -217,7 +217,11 @@ static void launch_pl_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t
     switch (bm) {
         case 256: launch_pl_tile<256, 256, MODE, 64, 2, 2, FLAGS>(p, stream); break;
         case 192:
+            // the per-route-rows launches (forward rows, dx) share the DMA
+            // issue between the wave groups: dx on Mixtral 889-904 -> 759-763
+            // us; on the 256- and 128-row tiles sharing measured 1-5 % slower
             if (avg < 192) launch_pl_tile<192, 256, MODE, 64, 3, 2, FLAGS, true>(p, stream);
+            else if constexpr (MODE == kDownRows) launch_pl_tile<192, 256, MODE, 64, 3, 2, FLAGS | kFlagSplitDma, false>(p, stream);
             else launch_pl_tile<192, 256, MODE, 64, 3, 2, FLAGS, false>(p, stream);
             break;
         case 128: launch_pl_tile<128, 256, MODE, 64, 4, 2, FLAGS>(p, stream); break;
