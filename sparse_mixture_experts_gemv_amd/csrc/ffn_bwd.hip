@@ -72,18 +72,23 @@ __global__ __launch_bounds__(256) void ffn_bwd_gate_reduce_kernel(const float *_
 }
 
 // Tile rows of the dh GEMM: 192 for experts of ~100-190 rows (one tile per
-// expert, so its W2 streams once; the short-tile path skips missing rows),
-// else 128 / 64 / 32.
+// expert, so its W2 streams once; the short-tile path skips missing rows)
+// and, since the 192-row tile shares its DMA issue between the wave groups,
+// for experts of 384 rows and more (Mixtral dh 1095-1110 -> 1076-1081 us,
+// Qwen2 S = 4096 811-822 -> 726-740 us against 128-row tiles); else 128 / 64
+// / 32.
 static int bwd_pick_bm(int64_t avg) {
+    if (avg >= 384) return 192;
     if (avg >= 192) return 128;
     if (avg >= 96) return 192;
     if (avg >= 48) return 64;
     return 32;
 }
 
-// The input-gradient GEMM (K = 2F) also takes 192-row tiles once experts are
-// large (measured on Mixtral: 1.82 against 2.13 ms with 128-row tiles, while
-// the dh GEMM, K = D, is faster with 128 rows).
+// The input-gradient GEMM (K = 2F) takes 192-row tiles once experts are
+// large (measured on Mixtral: 1.82 against 2.13 ms with 128-row tiles); from
+// 192 to 383 rows per expert it keeps 128-row tiles (GPT-OSS dx 1388-1390
+// against 1508-1514 us with 192 rows).
 static int bwd_pick_bm_dx(int64_t avg) { return avg >= 384 ? 192 : bwd_pick_bm(avg); }
 
 FfnBwdPlan ffn_bwd_plan(int64_t S, int64_t D, int64_t F, int64_t E, int64_t k) {
