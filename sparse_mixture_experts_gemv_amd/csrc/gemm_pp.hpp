@@ -364,7 +364,8 @@ __device__ __forceinline__ void pp_tile(const GemmParams &p, char *smem, int mt,
         // block, the opaque move keeps the compiler from hoisting each into
         // a register of its own, so the constants go into the reads' offset
         // fields (with few, the hoisted form schedules better)
-        constexpr bool B_LANE_REG = !BT && KK * NB >= 4;
+        constexpr bool B_LANE_REG = !BT && (KK * NB >= 4 || (BN == 256 && KK == 2 && BM == 256 && STAGES == 3));
+        // (the 256 x 256 x 64 3-deep tile also needs it: 14 spilled VGPRs with it, 74 without)
         int b_lane[BT ? 1 : NT];
         if constexpr (!BT) {
 #pragma unroll

@@ -215,7 +215,12 @@ static void launch_pl_tile(const GemmParams &p0, hipStream_t stream) {
 template <int MODE, int FLAGS>
 static void launch_pl_gemm(int bm, int64_t avg, const GemmParams &p, hipStream_t stream) {
     switch (bm) {
-        case 256: launch_pl_tile<256, 256, MODE, 64, 2, 2, FLAGS>(p, stream); break;
+        case 256:
+            // the gate+up tile's ring (3-deep weights, 2-deep rows, DMA
+            // shared by the wave groups): Mixtral forward 847-854 -> 811-824
+            // us against the 2/2 ring with group 0 issuing
+            launch_pl_tile<256, 256, MODE, 64, 3, 2, FLAGS | kFlagSplitDma>(p, stream);
+            break;
         case 192:
             // the per-route-rows launches (forward rows, dx) share the DMA
             // issue between the wave groups: dx on Mixtral 889-904 -> 759-763
