@@ -25,7 +25,9 @@
 // of its ring (both groups finished reading it at least one phase earlier),
 // spread among its fragment reads, so up to STAGES - 1 steps of weights are
 // in flight per CU. Either group 0 issues both rings and, at the end of its
-// MFMA phase, waits until step k + 1 has landed; or (the gate+up tiles)
+// MFMA phase, waits until step k + 1 has landed; or (the gate+up tiles and
+// the launches that pass kFlagSplitDma: the 64-deep down, input-gradient
+// and ParallelLinear tiles listed at pp_dma_split)
 // group 0 issues A and waits for it there, and group 1 issues B and waits,
 // at the end of its read phase, for the B of step k + 1. Both waits come
 // before the barrier that opens step k + 1 to readers. The DMA is plain
@@ -122,8 +124,12 @@ struct PPGeom {
 // 32-deep tiles sharing was 1-3 % slower, but on its 192 x 256 tile with
 // 64-deep k-steps (3/2 rings) it pays: Mixtral 885-888 -> 842-844 us,
 // Qwen2 S = 4096 748-762 -> 693-696 us, which beats the 32-deep 4/4 tile
-// without sharing; launches opt in with kFlagSplitDma (the 128-row and
-// short-tile down launches measured 0-1 % slower with it).
+// without sharing. Launches opt in with kFlagSplitDma: that down tile, the
+// backward's 192- and 128-row transposed-weight tiles, the ParallelLinear
+// input-gradient 192-row tile and its 256-row forward tile (with a 3-deep
+// weight ring). The 128-row and short-tile down launches, the router's
+// logits tile, the decode-size tiles and the stream-K down GEMM measured
+// 0-1 % slower or unchanged with it.
 constexpr bool pp_dma_split(int mode, int flags) {
     return mode == kGateUp || mode == kGateUpSave || (flags & kFlagSplitDma) != 0;
 }
